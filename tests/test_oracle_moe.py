@@ -1,0 +1,149 @@
+"""Pins of the oracle's W4A8 MoE layer against closed forms, exact integer cases, a
+plain dense two-expert computation, and the unquantized layer within a rigorous
+error bound (no GPU)."""
+import math
+
+import numpy as np
+import pytest
+from scipy.special import expit
+from scipy.stats import norm
+
+import synth
+from oracle import (ACT_GELU_ERF, ACT_GELU_TANH, ACT_SILU, activation, act_lipschitz,
+                    bf16_to_f32, bf16_to_f64, e4m3_decode, moe_error_bound, moe_forward,
+                    moe_reference_unquantized, quantize_static, static_scale, w4_pack,
+                    w4_quantize, w4_unpack_codes, route_top2)
+
+
+def test_activation_closed_forms():
+    g = np.linspace(-12, 12, 2001)
+    assert np.allclose(activation(g, ACT_SILU), g * expit(g), rtol=1e-13, atol=1e-15)
+    assert np.allclose(activation(g, ACT_GELU_ERF), g * norm.cdf(g), rtol=1e-12, atol=1e-15)
+    for a in (ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH):
+        assert activation(0.0, a) == 0.0
+        assert abs(activation(40.0, a) - 40.0) < 1e-9
+        assert abs(activation(-40.0, a)) < 1e-9
+    # the tanh form stays within 1e-3 of the erf form
+    assert np.max(np.abs(activation(g, ACT_GELU_TANH) - activation(g, ACT_GELU_ERF))) < 1e-3
+
+
+def test_lipschitz_constants():
+    # silu' peaks at about 1.0998 near g = 2.4; gelu_erf' = Phi(g) + g phi(g) peaks at g = sqrt 2
+    assert abs(act_lipschitz(ACT_SILU) - 1.0998) < 1e-3
+    peak = norm.cdf(math.sqrt(2)) + math.sqrt(2) * norm.pdf(math.sqrt(2))
+    assert act_lipschitz(ACT_GELU_ERF) >= peak and act_lipschitz(ACT_GELU_ERF) - peak < 1e-4
+
+
+def test_static_scale_and_quantize():
+    assert static_scale(448.0) == np.float32(1.0)
+    assert static_scale(4.48) == np.float32(np.float32(4.48) / np.float32(448.0))
+    v = np.array([1.0, -2.0, 448.0, 500.0, 1e-9], np.float32)
+    assert quantize_static(v, 1.0).tolist() == [0x38, 0xC0, 0x7E, 0x7E, 0x00]
+    with pytest.raises(ValueError):
+        quantize_static(v, 0.0)
+
+
+def _layer_inputs(cfg):
+    x = synth.activations(cfg)
+    logits = synth.router_logits(cfg)
+    w13 = synth.moe_weights(cfg, "w13")
+    w2 = synth.moe_weights(cfg, "w2")
+    return x, logits, w13, w2
+
+
+def _calibrate(cfg, x, logits, p13, p2):
+    s_x = static_scale(np.max(np.abs(bf16_to_f32(x))))
+    pre = moe_forward(x, logits, s_x, p13, p2, cfg.act, np.float32(1.0), cfg.out_f32)
+    s_a = static_scale(np.max(np.abs(pre["a"])))
+    return s_x, s_a
+
+
+def test_integer_case_gate_up_exact():
+    """x and w integer-valued, every row's max |w| = 7 and s_x = 1: the gate|up values
+    equal an integer matrix product exactly."""
+    rng = np.random.default_rng(21)
+    T, H, I, E = 6, 64, 32, 3
+    xi = rng.integers(-16, 17, size=(T, H))
+    w13i = rng.integers(-7, 8, size=(E, 2 * I, H))
+    w13i[:, :, 0] = 7
+    w2i = rng.integers(-7, 8, size=(E, H, I))
+    w2i[:, :, 0] = -7
+    x = synth.f32_to_bf16_bits(xi.astype(np.float32))
+    p13 = w4_pack(synth.f32_to_bf16_bits(w13i.astype(np.float32)))
+    p2 = w4_pack(synth.f32_to_bf16_bits(w2i.astype(np.float32)))
+    assert np.all(p13[1] == 1.0) and np.all(p2[1] == 1.0)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    r = moe_forward(x, logits, np.float32(1.0), p13, p2, ACT_SILU, np.float32(0.5), True)
+    for i, row in enumerate(r["rows"]):
+        e = int(np.searchsorted(r["offsets"], row, side="right") - 1)
+        t = r["sorted_pair"][row] // 2
+        assert np.array_equal(r["h"][i], w13i[e] @ xi[t])
+    assert np.array_equal(r["x_codes"], quantize_static(xi[r["x_codes_tokens"]].astype(np.float32), 1.0))
+
+
+def test_two_experts_dense_textbook():
+    """E = 2: every token uses both experts, so the layer is w0 FFN_a(x) + w1 FFN_b(x)
+    computed densely without any sorting."""
+    cfg = synth.custom_moe("e2", T=12, H=128, I=256, E=2, act=ACT_GELU_ERF, w_cfg=31, x_cfg=31)
+    x, logits, w13, w2 = _layer_inputs(cfg)
+    p13, p2 = w4_pack(w13), w4_pack(w2)
+    s_x, s_a = _calibrate(cfg, x, logits, p13, p2)
+    r = moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, True)
+    xt = e4m3_decode(quantize_static(bf16_to_f32(x), s_x)) * np.float64(s_x)
+    ids, w = route_top2(logits)
+    out = np.zeros((cfg.T, cfg.H))
+    for e in range(2):
+        W13 = w4_unpack_codes(p13[0][e]).astype(np.float64) * p13[1][e].astype(np.float64)[:, None]
+        W2 = w4_unpack_codes(p2[0][e]).astype(np.float64) * p2[1][e].astype(np.float64)[:, None]
+        h = xt @ W13.T
+        a = activation(h[:, :cfg.I], cfg.act) * h[:, cfg.I:]
+        at = e4m3_decode(quantize_static(a.astype(np.float32), s_a)) * np.float64(s_a)
+        y = at @ W2.T
+        we = np.where(ids[:, 0] == e, w[:, 0], w[:, 1])
+        out += we[:, None] * y
+    assert np.allclose(r["out"], out, rtol=1e-12, atol=1e-12 * np.abs(out).max())
+
+
+@pytest.mark.parametrize("cfg", [synth.TINY,
+                                 synth.custom_moe("tiny_gelu", 16, 256, 512, 4, act=ACT_GELU_ERF,
+                                                  w_sigma=0.015, logit_sigma=1.5, w_cfg=41, x_cfg=41)])
+def test_quantized_layer_within_rigorous_bound_of_unquantized(cfg):
+    x, logits, w13, w2 = _layer_inputs(cfg)
+    p13, p2 = w4_pack(w13), w4_pack(w2)
+    s_x, s_a = _calibrate(cfg, x, logits, p13, p2)
+    r = moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32)
+    ref = moe_reference_unquantized(x, logits, w13, w2, cfg.act)
+    bound = moe_error_bound(x, logits, w13, w2, cfg.act, s_x, s_a)
+    err = np.abs(r["out"] - ref)
+    assert np.all(err <= bound * (1 + 1e-9) + 1e-12)
+    rel = np.linalg.norm(r["out"] - ref) / np.linalg.norm(ref)
+    assert 0.01 < rel < 0.35, rel
+
+
+def test_token_subset_matches_full_run():
+    cfg = synth.custom_moe("sub", T=40, H=128, I=256, E=8, w_cfg=51, x_cfg=51)
+    x, logits, w13, w2 = _layer_inputs(cfg)
+    p13, p2 = w4_pack(w13), w4_pack(w2)
+    full = moe_forward(x, logits, np.float32(0.01), p13, p2, cfg.act, np.float32(0.001), True)
+    toks = np.array([3, 17, 39, 0])
+    sub = moe_forward(x, logits, np.float32(0.01), p13, p2, cfg.act, np.float32(0.001), True,
+                      tokens=toks)
+    assert np.array_equal(sub["out"], full["out"][toks])
+    provider = lambda e: (p13[0][e], p13[1][e])
+    sub2 = moe_forward(x, logits, np.float32(0.01), provider, p2, cfg.act, np.float32(0.001), True,
+                       tokens=toks)
+    assert np.array_equal(sub2["out"], sub["out"])
+
+
+def test_pair_rows_and_combine_plumbing():
+    """The output of token t only combines the rows of its own two pairs, in slot order."""
+    cfg = synth.custom_moe("plumb", T=9, H=128, I=128, E=4, w_cfg=61, x_cfg=61)
+    x, logits, w13, w2 = _layer_inputs(cfg)
+    p13, p2 = w4_pack(w13), w4_pack(w2)
+    r = moe_forward(x, logits, np.float32(0.01), p13, p2, cfg.act, np.float32(0.001), True)
+    for t in range(cfg.T):
+        r0 = np.nonzero(r["rows"] == r["pair_pos"][2 * t])[0][0]
+        r1 = np.nonzero(r["rows"] == r["pair_pos"][2 * t + 1])[0][0]
+        assert r["sorted_pair"][r["rows"][r0]] == 2 * t
+        expect = r["weights"][t, 0] * r["y"][r0] + r["weights"][t, 1] * r["y"][r1]
+        assert np.array_equal(r["out"][t], expect)
