@@ -44,19 +44,21 @@ def e4m3_decode(codes) -> np.ndarray:
 
 
 def e4m3_encode(v) -> np.ndarray:
-    """Nearest E4M3 code of each (finite) value; ties to even code; saturating.
+    """Nearest E4M3 code of each value; ties to even code; saturating (an fp32 quotient
+    that overflowed to +-inf saturates too). NaN is rejected.
 
     ``v`` is read exactly as fp64 (pass the fp32 quotient the method forms).
     """
     v = np.asarray(v, dtype=np.float64)
-    if not np.all(np.isfinite(v)):
-        raise ValueError("e4m3_encode: non-finite input")
+    if np.any(np.isnan(v)):
+        raise ValueError("e4m3_encode: NaN input")
     a = np.abs(v)
     hi = np.searchsorted(_MAGS, a, side="left")          # first magnitude >= a
     hi = np.clip(hi, 1, 0x7E)
     lo = hi - 1
-    d_lo = a - _MAGS[lo]                                   # exact in fp64
-    d_hi = _MAGS[hi] - a
+    with np.errstate(invalid="ignore"):                    # inf - inf on saturated lanes
+        d_lo = a - _MAGS[lo]                               # exact in fp64
+        d_hi = _MAGS[hi] - a
     take_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
     code = np.where(take_hi, hi, lo)
     code = np.where(a >= E4M3_MAX, 0x7E, code)             # saturate

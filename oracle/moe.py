@@ -71,7 +71,8 @@ def quantize_static(v, s) -> np.ndarray:
     s = np.float32(s)
     if not s > 0:
         raise ValueError("static scale must be positive")
-    q = (np.asarray(v, dtype=np.float32) / s).astype(np.float32)   # correctly rounded
+    with np.errstate(over="ignore"):                            # overflow -> inf -> saturates
+        q = (np.asarray(v, dtype=np.float32) / s).astype(np.float32)   # correctly rounded
     return e4m3_encode(q)
 
 

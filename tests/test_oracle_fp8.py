@@ -113,6 +113,7 @@ def test_saturation_and_signed_zero():
     assert e4m3_encode(-1e6) == 0xFE
     assert e4m3_encode(-0.0) == 0x80
     assert e4m3_encode(0.0) == 0x00
+    assert e4m3_encode(float("inf")) == 0x7E and e4m3_encode(float("-inf")) == 0xFE
     with pytest.raises(ValueError):
         e4m3_encode(float("nan"))
 
