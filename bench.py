@@ -1,0 +1,261 @@
+"""Benchmark of the W4A8 MoE layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one forward of the layer over one batch of synthetic tokens: moe_route_sort,
+fp8_quant_static (x -> E4M3), moe_gemm1_w4a8, moe_gemm2_w4a8 (down + combine). Inputs
+(packed weights, scales, x, logits) are resident in HBM before the timed region. The
+packed weights are rotated over several copies when one copy would fit in the 256 MB
+Infinity Cache, so that the HBM stream is measured. w4_pack (load time) and the block-FP8
+GEMV are timed separately and reported in the same JSON line.
+
+Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense OCP-FP8 MFMA, published
+METRIC = "MoE layer tokens/s + % HBM peak (decode T=32), % fp8 MFMA peak (prefill)"
+ACT_NAMES = {synth.ACT_SILU: "silu", synth.ACT_GELU_ERF: "gelu_erf", synth.ACT_GELU_TANH: "gelu_tanh"}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_decode", choices=sorted(synth.MOE_CONFIGS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-gemv", action="store_true", help="skip timing the block-FP8 GEMVs")
+    return ap.parse_args()
+
+
+def static_scales(name):
+    d = json.load(open(os.path.join(ROOT, "tests", "golden", "static_scales.json")))[name]
+    return np.float32(float.fromhex(d["s_x_hex"])), np.float32(float.fromhex(d["s_a_hex"]))
+
+
+def bf16_dev(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def moe_bytes(cfg, counts):
+    """Algorithmic HBM bytes of the layer and of the gate|up call (touched experts only)."""
+    touched = int(np.count_nonzero(counts))
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    P = 2 * T
+    w13 = touched * (2 * I * H // 2 + 2 * I * 4)
+    w2 = touched * (H * I // 2 + H * 4)
+    gemm1 = w13 + T * H + P * I                      # packed w13 + scales, x codes in, a codes out
+    layer = w13 + w2 + T * H * 2 + T * E * 4 + T * H * (4 if cfg.out_f32 else 2)
+    return layer, gemm1, touched
+
+
+def cpu_baseline(cfg, s_x, s_a, ids):
+    """The oracle on a bounded sample of the same workload: the tokens routed to the most
+    common expert pair of the batch (their two experts' weights packed by the oracle,
+    untimed); the timed part is the oracle's layer forward of those tokens."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas_threads = 1
+    x = synth.activations(cfg)
+    logits = synth.router_logits(cfg)
+    pairs = [tuple(sorted(map(int, r))) for r in ids]
+    best = max(set(pairs), key=pairs.count)
+    toks = np.array([t for t, p in enumerate(pairs) if p == best], dtype=np.int64)
+    packed13 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w13", e)) for e in best}
+    packed2 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w2", e)) for e in best}
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, logits, s_x, lambda e: packed13[e], lambda e: packed2[e], cfg.act, s_a, cfg.out_f32,
+                       tokens=toks, E=cfg.E)
+    dt = time.perf_counter() - t0
+    return {"value": float(len(toks) / dt), "unit": "tokens/s",
+            "cores": int(max(1, blas_threads)), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
+            "sample": f"{len(toks)} of {cfg.T} tokens (those routed to experts {best[0]} and {best[1]}), "
+                      f"full oracle forward (fp64, int4 unpack, exact sums); {dt:.2f} s"}
+
+
+def bench_block_gemv(torch, W, dev, reps=16, iters=50):
+    """block-FP8 GEMV at the projection shapes; weights rotated over `reps` copies."""
+    out = {}
+    for cfg in synth.BLOCK_CONFIGS.values():
+        w = bf16_dev(torch, synth.block_weights(cfg), dev)
+        q, S = W.fp8_block_quant(w)
+        del w
+        qs = [q.clone() for _ in range(reps)]
+        x = bf16_dev(torch, synth.block_activations(cfg), dev)
+        y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
+        for i in range(5):
+            W.fp8_block_linear(x, qs[i % reps], S, out=y)
+        st = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(st)
+        for i in range(iters):
+            W.fp8_block_linear(x, qs[i % reps], S, out=y)
+        ev[1].record(st)
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+        nbytes = cfg.N * cfg.K + S.numel() * 4 + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2
+        out[cfg.name] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+                         "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del qs
+    return out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the layer on one GPU's share); "
+              "--gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import w4a8_moe_amd as W
+
+    cfg = synth.MOE_CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    s_x, s_a = static_scales(cfg.name)
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+
+    # ---- load: bf16 weights -> w4_pack on the GPU (timed separately), rotation copies
+    w13b = bf16_dev(torch, synth.moe_weights(cfg, "w13"), dev)
+    w2b = bf16_dev(torch, synth.moe_weights(cfg, "w2"), dev)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    w13, s13 = W.w4_pack(w13b)
+    w2, s2 = W.w4_pack(w2b)
+    e1.record()
+    torch.cuda.synchronize()
+    pack_ms = e0.elapsed_time(e1)
+    pack_bytes = (w13b.numel() + w2b.numel()) * 2.5 + (s13.numel() + s2.numel()) * 4
+    del w13b, w2b
+    packed_bytes = (w13.numel() + w2.numel()) * 4
+    copies = max(1, int(np.ceil(768e6 / packed_bytes))) if packed_bytes < 768e6 else 1
+    W13 = [w13] + [w13.clone() for _ in range(copies - 1)]
+    W2 = [w2] + [w2.clone() for _ in range(copies - 1)]
+
+    x = bf16_dev(torch, synth.activations(cfg), dev)
+    logits = torch.from_numpy(synth.router_logits(cfg)).to(dev)
+    xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    a = torch.empty((2 * T, I), dtype=torch.uint8, device=dev)
+    out = torch.empty((T, H), dtype=torch.float32 if cfg.out_f32 else torch.bfloat16, device=dev)
+    ws1 = torch.empty(max(256, W.workspace_bytes(W.OP_GEMM1, T, H, I, E)), dtype=torch.uint8, device=dev)
+    ws2 = torch.empty(max(256, W.workspace_bytes(W.OP_GEMM2, T, H, I, E)), dtype=torch.uint8, device=dev)
+    ro = W.route_outputs(T, E, dev)
+    od = "f32" if cfg.out_f32 else "bf16"
+
+    def route():
+        W.moe_route_sort(logits, out=ro)
+
+    def quant():
+        W.fp8_quant_static(x, s_x, out=xq)
+
+    def gemm1(i):
+        W.moe_gemm1_w4a8(xq, s_x, W13[i % copies], s13, ro["offsets"], ro["sorted_pair"], cfg.act, s_a, ws=ws1,
+                         out=a)
+
+    def gemm2(i):
+        W.moe_gemm2_w4a8(a, s_a, W2[i % copies], s2, ro["offsets"], ro["pair_pos"], ro["weights"], od, ws=ws2,
+                         out=out)
+
+    def step(i):
+        route(); quant(); gemm1(i); gemm2(i)
+
+    # eager reference step, then one captured HIP graph per weight copy (launch overhead
+    # of the Python binding stays out of the timed region); the replay must match eager
+    step(0)
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    counts = ro["counts"].cpu().numpy()
+    ids = ro["ids"].cpu().numpy()
+    graphs = []
+    for c in range(copies):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(c)
+        graphs.append(g)
+    for i in range(args.warmup):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    if not torch.equal(out, ref_out):
+        raise RuntimeError("graph replay differs from the eager step")
+
+    # ---- timed region: K steps, wall clock between two synchronizations
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % copies].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    # ---- per-call duration: back-to-back launches of one call between two HIP events on
+    #      the stream the library launches on
+    st = torch.cuda.current_stream()
+
+    def per_launch_us(fn, n=max(20, args.steps)):
+        for i in range(3):
+            fn(i)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record(st)
+        for i in range(n):
+            fn(i)
+        ev1.record(st)
+        torch.cuda.synchronize()
+        return ev0.elapsed_time(ev1) * 1e3 / n
+
+    per_call = {"route_sort": per_launch_us(lambda i: route()), "quant_x": per_launch_us(lambda i: quant()),
+                "gemm1": per_launch_us(gemm1), "gemm2_combine": per_launch_us(gemm2)}
+    layer_bytes, gemm1_bytes, touched = moe_bytes(cfg, counts)
+    layer_us = ms_per_step * 1e3
+    g1_gbs = gemm1_bytes / per_call["gemm1"] / 1e3
+    result = {
+        "metric": METRIC,
+        "value": round(T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "e4m3",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": 2,
+                   "activation": ACT_NAMES[cfg.act], "out": "fp32" if cfg.out_f32 else "bf16",
+                   "weight_copies_rotated": copies, "experts_touched": touched},
+        "layer_hbm_frac": round(layer_bytes / (layer_us * 1e3) / HBM_PEAK_GBS, 4),
+        "layer_bytes": int(layer_bytes),
+        "calls_us": {k: round(v, 2) for k, v in per_call.items()},
+        "roofline": {"kernel": "moe_gemm1_w4a8 (moe_decode_kernel<gate|up>)", "bound": "hbm",
+                     "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(gemm1_bytes)},
+        "w4_pack": {"ms": round(pack_ms, 3), "GB/s": round(pack_bytes / pack_ms / 1e6, 1)},
+    }
+    if not args.no_block_gemv:
+        result["block_fp8_gemv"] = bench_block_gemv(torch, W, dev)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, s_x, s_a, ids)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

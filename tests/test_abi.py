@@ -1,0 +1,129 @@
+"""The C-ABI library loads, exports every declared entry point, and rejects bad arguments
+on the host before any HIP call (no GPU needed: every call below fails validation)."""
+import ctypes
+
+import pytest
+
+import w4a8_moe_amd as W
+
+A = 0x10000          # a fake, 16-byte aligned device address (never dereferenced)
+U = 0x10008          # a fake, misaligned address
+
+
+@pytest.fixture(scope="module")
+def L():
+    return W.lib()
+
+
+def test_exports_every_declared_function(L):
+    names = W.header_functions()
+    assert set(names) == {"w4_pack", "fp8_quant_static", "moe_route_sort", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
+                          "fp8_block_quant", "fp8_block_linear", "w4a8_workspace_bytes", "w4a8_status_str"}
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings(L):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7):
+        assert W.status_str(code) and W.status_str(code) != "unknown status"
+    assert W.status_str(-99) == "unknown status"
+
+
+def test_w4_pack_validation(L):
+    assert L.w4_pack(None, 1, 16, 64, A, A, None) == W.ERR_NULL
+    assert L.w4_pack(A, 1, 16, 60, A, A, None) == W.ERR_SHAPE          # K % 8
+    assert L.w4_pack(A, 0, 16, 64, A, A, None) == W.ERR_SHAPE
+    assert L.w4_pack(A, 1, 16, 4, A, A, None) == W.ERR_SHAPE
+    assert L.w4_pack(U, 1, 16, 64, A, A, None) == W.ERR_ALIGN
+    assert L.w4_pack(A, 1, 16, 64, A, U, None) == W.ERR_ALIGN
+
+
+def test_fp8_quant_validation(L):
+    assert L.fp8_quant_static(A, 16, 0.0, A, None) == W.ERR_ARG
+    assert L.fp8_quant_static(A, 16, float("nan"), A, None) == W.ERR_ARG
+    assert L.fp8_quant_static(A, 16, float("inf"), A, None) == W.ERR_ARG
+    assert L.fp8_quant_static(A, -1, 1.0, A, None) == W.ERR_SHAPE
+    assert L.fp8_quant_static(None, 16, 1.0, A, None) == W.ERR_NULL
+    assert L.fp8_quant_static(A, 16, 1.0, U, None) == W.ERR_ALIGN
+    assert L.fp8_quant_static(None, 0, 1.0, None, None) == W.OK        # empty: nothing enqueued
+
+
+def test_route_sort_validation(L):
+    f = L.moe_route_sort
+    assert f(A, 8, 1, A, A, A, A, A, A, None, 0, None) == W.ERR_SHAPE         # E < 2
+    assert f(A, 8, 257, A, A, A, A, A, A, None, 0, None) == W.ERR_SHAPE       # E > 256
+    assert f(A, -1, 8, A, A, A, A, A, A, None, 0, None) == W.ERR_SHAPE
+    assert f(A, (1 << 22) + 1, 8, A, A, A, A, A, A, None, 0, None) == W.ERR_SHAPE
+    assert f(None, 8, 8, A, A, A, A, A, A, None, 0, None) == W.ERR_NULL
+    assert f(A, 8, 8, A, A, A, A, U, A, None, 0, None) == W.ERR_ALIGN
+    need = W.workspace_bytes(W.OP_ROUTE_SORT, 5000, 0, 0, 8)
+    assert need > 0 and W.workspace_bytes(W.OP_ROUTE_SORT, 256, 0, 0, 8) == 0
+    assert f(A, 5000, 8, A, A, A, A, A, A, A, need - 1, None) == W.ERR_WORKSPACE
+    assert f(A, 5000, 8, A, A, A, A, A, A, None, need, None) == W.ERR_NULL
+
+
+def _g1(L, **kw):
+    a = dict(x=A, x_dtype=W.DT_E4M3, s_x=0.01, w13=A, s_w13=A, offsets=A, sorted_pair=A, T=32, H=256, I=512,
+             E=8, act=W.ACT_SILU, s_a=0.01, a_fp8=A, dbg=None, ws=None, ws_bytes=0)
+    a.update(kw)
+    return L.moe_gemm1_w4a8(a["x"], a["x_dtype"], a["s_x"], a["w13"], a["s_w13"], a["offsets"], a["sorted_pair"],
+                            a["T"], a["H"], a["I"], a["E"], a["act"], a["s_a"], a["a_fp8"], a["dbg"], a["ws"],
+                            a["ws_bytes"], None)
+
+
+def test_gemm1_validation(L):
+    assert _g1(L, H=200) == W.ERR_SHAPE
+    assert _g1(L, I=100) == W.ERR_SHAPE
+    assert _g1(L, E=1) == W.ERR_SHAPE
+    assert _g1(L, T=-3) == W.ERR_SHAPE
+    assert _g1(L, act=7) == W.ERR_ARG
+    assert _g1(L, x_dtype=W.DT_F32) == W.ERR_ARG
+    assert _g1(L, s_x=0.0) == W.ERR_ARG
+    assert _g1(L, s_a=-1.0) == W.ERR_ARG
+    assert _g1(L, w13=None) == W.ERR_NULL
+    assert _g1(L, a_fp8=U) == W.ERR_ALIGN
+    assert _g1(L, dbg=U) == W.ERR_ALIGN
+    need = W.workspace_bytes(W.OP_GEMM1_BF16, 32, 256, 512, 8)
+    assert need >= 32 * 256 and W.workspace_bytes(W.OP_GEMM1, 32, 256, 512, 8) == 0
+    assert _g1(L, x_dtype=W.DT_BF16, ws=A, ws_bytes=need - 1) == W.ERR_WORKSPACE
+    assert _g1(L, T=0) == W.OK                                   # empty: nothing enqueued
+
+
+def _g2(L, **kw):
+    a = dict(a=A, s_a=0.01, w2=A, s_w2=A, offsets=A, pair_pos=A, topk_w=A, T=32, H=256, I=512, E=8,
+             dt=W.DT_BF16, out=A, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.moe_gemm2_w4a8(a["a"], a["s_a"], a["w2"], a["s_w2"], a["offsets"], a["pair_pos"], a["topk_w"],
+                            a["T"], a["H"], a["I"], a["E"], a["dt"], a["out"], a["ws"], a["ws_bytes"], None)
+
+
+def test_gemm2_validation(L):
+    assert _g2(L, I=384 + 64) == W.ERR_SHAPE
+    assert _g2(L, dt=W.DT_E4M3) == W.ERR_ARG
+    assert _g2(L, s_a=float("nan")) == W.ERR_ARG
+    assert _g2(L, topk_w=None) == W.ERR_NULL
+    assert _g2(L, out=U) == W.ERR_ALIGN
+    need = W.workspace_bytes(W.OP_GEMM2, 32, 256, 512, 8)
+    assert need >= 2 * 32 * 256 * 4
+    assert _g2(L, ws_bytes=need - 1) == W.ERR_WORKSPACE
+    assert _g2(L, ws=None, ws_bytes=need) == W.ERR_NULL
+    assert _g2(L, T=0) == W.OK
+
+
+def test_block_validation(L):
+    assert L.fp8_block_quant(None, 128, 128, A, A, None) == W.ERR_NULL
+    assert L.fp8_block_quant(A, 128, 100, A, A, None) == W.ERR_SHAPE
+    assert L.fp8_block_quant(A, 128, 128, U, A, None) == W.ERR_ALIGN
+    f = L.fp8_block_linear
+    assert f(A, A, A, 0, 256, 256, A, None, 0, None) == W.ERR_SHAPE
+    assert f(A, A, A, 17, 256, 256, A, None, 0, None) == W.ERR_SHAPE
+    assert f(A, A, A, 1, 250, 256, A, None, 0, None) == W.ERR_SHAPE
+    assert f(A, A, A, 1, 256, 200, A, None, 0, None) == W.ERR_SHAPE
+    assert f(A, A, A, 16, 256, 4096, A, None, 0, None) == W.ERR_UNSUPPORTED
+    assert f(A, A, U, 1, 256, 256, A, None, 0, None) == W.ERR_ALIGN
+    assert f(None, A, A, 1, 256, 256, A, None, 0, None) == W.ERR_NULL
+
+
+def test_workspace_bad_args(L):
+    assert W.workspace_bytes(99, 1, 1, 1, 1) == 0
+    assert W.workspace_bytes(W.OP_GEMM2, 32, 100, 512, 8) == 0

@@ -1,0 +1,217 @@
+"""Parity of the HIP library (through the C ABI) with the CPU oracle on seeded inputs.
+
+Bit-exact: packing, scales, fp8 activation codes, routing ids, counts, offsets,
+sorted_pair, pair_pos, block-FP8 codes and scales. Tolerances: topk_w 1e-6; gate|up
+1e-4 x row max; final outputs 1e-2 x max|ref| with at most 0.1% of elements above
+1e-3 x max|ref| (bf16 outputs against the oracle's bf16-rounded result).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a8_moe_amd as W
+from tests.gpu_util import (assert_codes_consistent, assert_final_close, assert_gateup_close, bf16_bits_to_f64,
+                            bf16_dev, f32_dev, host, same_codes, torch, u8_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _all_bf16_finite():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    v = bf16_bits_to_f64(bits)
+    return bits[np.isfinite(v)]
+
+
+# ----------------------------------------------------------------- fp8 activation quant
+
+@pytest.mark.parametrize("scale", [1.0, 0.0123, 3.7e-3, 7.25, 2.0 ** -20])
+def test_fp8_quant_exhaustive_bf16(scale):
+    bits = _all_bf16_finite()
+    got = host(W.fp8_quant_static(bf16_dev(bits), np.float32(scale)))
+    ref = oracle.quantize_static(oracle.bf16_to_f32(bits), np.float32(scale))
+    assert same_codes(got, ref).all()
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 9, 1000, 4099])
+def test_fp8_quant_tails(n):
+    rng = np.random.default_rng(n)
+    bits = synth.f32_to_bf16_bits(rng.standard_normal(n).astype(np.float32) * 3)
+    got = host(W.fp8_quant_static(bf16_dev(bits), np.float32(0.01)))
+    assert same_codes(got, oracle.quantize_static(oracle.bf16_to_f32(bits), np.float32(0.01))).all()
+
+
+# ----------------------------------------------------------------------------- w4_pack
+
+@pytest.mark.parametrize("E,N,K", [(1, 1, 8), (2, 48, 64), (3, 17, 264), (2, 5, 4096 + 8)])
+def test_w4_pack_bit_exact(E, N, K):
+    rng = np.random.default_rng(E * 1000 + N + K)
+    w = synth.f32_to_bf16_bits((rng.standard_normal((E, N, K)) * 0.02).astype(np.float32))
+    w[0, 0, :] = 0                                           # an all-zero row
+    if N > 2:
+        w[-1, 2, :] = synth.f32_to_bf16_bits(rng.integers(-7, 8, K).astype(np.float32))
+    packed, scale = W.w4_pack(bf16_dev(w))
+    ref_p, ref_s = oracle.w4_pack(w)
+    assert np.array_equal(host(scale), ref_s)
+    assert np.array_equal(host(packed), ref_p)
+
+
+def test_w4_pack_tiny_layer():
+    cfg = synth.TINY
+    for which in ("w13", "w2"):
+        w = synth.moe_weights(cfg, which)
+        packed, scale = W.w4_pack(bf16_dev(w))
+        ref_p, ref_s = oracle.w4_pack(w)
+        assert np.array_equal(host(scale), ref_s) and np.array_equal(host(packed), ref_p)
+
+
+# ------------------------------------------------------------------------ route + sort
+
+def _check_route(logits):
+    T, E = logits.shape
+    r = W.moe_route_sort(f32_dev(logits))
+    ids, w = oracle.route_top2(logits)
+    counts, offsets, sp, pos = oracle.route_sort(ids, E)
+    if T:
+        assert np.array_equal(host(r["ids"]), ids)
+        assert np.max(np.abs(host(r["weights"]) - w)) <= 1e-6
+        assert np.array_equal(host(r["sorted_pair"]), sp)
+        assert np.array_equal(host(r["pair_pos"]), pos)
+    assert np.array_equal(host(r["counts"]), counts)
+    assert np.array_equal(host(r["offsets"]), offsets)
+    return r
+
+
+@pytest.mark.parametrize("T,E,sigma", [(16, 4, 1.0), (32, 8, 1.5), (1, 2, 1.0), (255, 8, 1.5), (256, 8, 1.5),
+                                       (257, 8, 1.5), (5000, 8, 1.5), (1000, 64, 1.0), (300, 256, 1.0),
+                                       (4097, 3, 2.0)])
+def test_route_sort_bit_exact(T, E, sigma):
+    rng = np.random.default_rng(T * 7 + E)
+    _check_route((rng.standard_normal((T, E)) * sigma).astype(np.float32))
+
+
+def test_route_sort_empty_and_ties():
+    _check_route(np.zeros((0, 8), np.float32))
+    l = np.array([[1, 2, 2, 0.5], [0, 0, 0, 0], [3, 1, 3, 3], [-1, 5, -1, -1], [7, 7, 7, 7]], np.float32)
+    _check_route(l)
+    rng = np.random.default_rng(5)
+    skew = rng.standard_normal((3000, 8)).astype(np.float32)
+    skew[:, 5] += 4.0                                          # one expert takes almost every token
+    _check_route(skew)
+    q = np.round(rng.standard_normal((600, 16)) * 2).astype(np.float32) / 2   # many equal logits
+    _check_route(q)
+
+
+def test_route_sort_deterministic():
+    rng = np.random.default_rng(9)
+    l = f32_dev(rng.standard_normal((4000, 8)).astype(np.float32))
+    a, b = W.moe_route_sort(l), W.moe_route_sort(l)
+    for k in ("ids", "weights", "counts", "offsets", "sorted_pair", "pair_pos"):
+        assert torch().equal(a[k], b[k])
+
+
+# ------------------------------------------------------------------------- MoE layer
+
+def _oracle_scales(cfg, x, logits, p13, p2):
+    s_x = oracle.static_scale(np.max(np.abs(oracle.bf16_to_f32(x))))
+    pre = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, np.float32(1.0), cfg.out_f32)
+    return s_x, oracle.static_scale(np.max(np.abs(pre["a"])))
+
+
+LAYER_CASES = [
+    synth.TINY,
+    synth.custom_moe("ragged_k", T=32, H=640, I=4736, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=201,
+                     x_cfg=201, logit_sigma=1.5),
+    synth.custom_moe("chunked", T=64, H=1152, I=1280, E=2, act=synth.ACT_SILU, w_cfg=202, x_cfg=202),
+    synth.custom_moe("three_tiles", T=40, H=512, I=512, E=3, act=synth.ACT_GELU_TANH, w_cfg=203, x_cfg=203),
+    synth.custom_moe("one_token", T=1, H=256, I=256, E=8, w_cfg=204, x_cfg=204),
+    synth.custom_moe("many_experts", T=24, H=256, I=384, E=32, w_cfg=205, x_cfg=205, out_f32=False),
+]
+
+
+@pytest.mark.parametrize("cfg", LAYER_CASES, ids=[c.name for c in LAYER_CASES])
+def test_moe_layer_parity(cfg):
+    x = synth.activations(cfg)
+    logits = synth.router_logits(cfg)
+    w13 = synth.moe_weights(cfg, "w13")
+    w2 = synth.moe_weights(cfg, "w2")
+    p13, p2 = oracle.w4_pack(w13), oracle.w4_pack(w2)
+    s_x, s_a = _oracle_scales(cfg, x, logits, p13, p2)
+    ref = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32)
+
+    gw13, gs13 = W.w4_pack(bf16_dev(w13))
+    gw2, gs2 = W.w4_pack(bf16_dev(w2))
+    assert np.array_equal(host(gw13), p13[0]) and np.array_equal(host(gs13), p13[1])
+    assert np.array_equal(host(gw2), p2[0]) and np.array_equal(host(gs2), p2[1])
+    r = W.moe_route_sort(f32_dev(logits))
+    assert np.array_equal(host(r["sorted_pair"]), ref["sorted_pair"])
+    xd = bf16_dev(x)
+    a, h = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a, debug=True)
+    assert_gateup_close(host(h), ref["h"])
+    assert_codes_consistent(host(a), ref["a_codes"], host(h), cfg.act, s_a, cfg.I)
+    # the pre-quantized x path gives identical bytes
+    xq = W.fp8_quant_static(xd, s_x)
+    a2 = W.moe_gemm1_w4a8(xq, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a)
+    assert torch().equal(a, a2)
+    out = W.moe_gemm2_w4a8(a, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"],
+                           "f32" if cfg.out_f32 else "bf16")
+    if cfg.out_f32:
+        assert_final_close(host(out), ref["out"].astype(np.float32))
+    else:
+        assert_final_close(bf16_bits_to_f64(host(out)), bf16_bits_to_f64(ref["out_rounded"]))
+    # determinism: a second run is byte-identical
+    a3 = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a)
+    out3 = W.moe_gemm2_w4a8(a3, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"],
+                            "f32" if cfg.out_f32 else "bf16")
+    assert torch().equal(a, a3) and torch().equal(out, out3)
+
+
+def test_integer_case_gate_up_bit_exact():
+    """Integer x and w, max |w| = 7 per row, s_x = 1: fp32 accumulation is exact in any
+    order, so gate|up must equal the integer product exactly."""
+    rng = np.random.default_rng(77)
+    T, H, I, E = 20, 384, 256, 4
+    xi = rng.integers(-16, 17, size=(T, H))
+    w13i = rng.integers(-7, 8, size=(E, 2 * I, H))
+    w13i[:, :, 3] = 7
+    x = synth.f32_to_bf16_bits(xi.astype(np.float32))
+    w13 = synth.f32_to_bf16_bits(w13i.astype(np.float32))
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    gw13, gs13 = W.w4_pack(bf16_dev(w13))
+    assert np.all(host(gs13) == 1.0)
+    r = W.moe_route_sort(f32_dev(logits))
+    a, h = W.moe_gemm1_w4a8(bf16_dev(x), 1.0, gw13, gs13, r["offsets"], r["sorted_pair"], W.ACT_SILU, 1.0,
+                            debug=True)
+    h = host(h)
+    sp, off = host(r["sorted_pair"]), host(r["offsets"])
+    for row in range(2 * T):
+        e = int(np.searchsorted(off, row, side="right") - 1)
+        assert np.array_equal(h[row], (w13i[e] @ xi[sp[row] // 2]).astype(np.float32)), row
+
+
+# -------------------------------------------------------------------------- block FP8
+
+@pytest.mark.parametrize("N,K", [(200, 400), (128, 128), (16, 2560)])
+def test_fp8_block_quant_bit_exact(N, K):
+    cfg = synth.custom_block("bq", M=1, N=N, K=K, cfg=300 + N)
+    w = synth.block_weights(cfg)
+    w[:3, :] = 0
+    if N >= 128 and K >= 128:
+        w[:128, :128] = 0                                    # a zero block
+    q, S = W.fp8_block_quant(bf16_dev(w))
+    rq, rS = oracle.fp8_block_quantize(w)
+    assert np.array_equal(host(S), rS)
+    assert same_codes(host(q), rq).all()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 384), (8, 400, 256), (16, 128, 2048), (3, 1024, 2560), (12, 64, 2560)])
+def test_fp8_block_linear_parity(M, N, K):
+    cfg = synth.custom_block("bl", M=M, N=N, K=K, cfg=400 + M)
+    w = synth.block_weights(cfg)
+    x = synth.block_activations(cfg)
+    codes, S = oracle.fp8_block_quantize(w)
+    y_ref, y_bits = oracle.fp8_block_linear(x, codes, S)
+    y = W.fp8_block_linear(bf16_dev(x), u8_dev(codes), f32_dev(S))
+    assert_final_close(bf16_bits_to_f64(host(y)), bf16_bits_to_f64(y_bits))
+    y2 = W.fp8_block_linear(bf16_dev(x), u8_dev(codes), f32_dev(S))
+    assert torch().equal(y, y2)

@@ -1,0 +1,231 @@
+// C-ABI host layer of libw4a8moe: argument validation (before any HIP call), workspace
+// sizing, launch planning, and the launches on the caller's stream. See
+// include/libw4a8moe.h for the contract of every entry point.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/libw4a8moe.h"
+#include "kernels.h"
+
+using namespace w4a8;
+
+namespace {
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool good_scale(float s) { return std::isfinite(s) && s > 0.0f; }
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int32_t launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? W4A8_OK : W4A8_ERR_HIP;
+}
+
+constexpr int64_t kMaxRouteTokens = int64_t(1) << 22;
+
+// Shapes shared by the MoE GEMM calls.
+int32_t check_moe_shape(int32_t T, int32_t H, int32_t I, int32_t E) {
+  if (T < 0 || T > kMaxRouteTokens) return W4A8_ERR_SHAPE;
+  if (E < 2 || E > W4A8_MAX_EXPERTS) return W4A8_ERR_SHAPE;
+  if (H <= 0 || I <= 0 || H % 128 != 0 || I % 128 != 0) return W4A8_ERR_SHAPE;
+  if ((int64_t)T * H >= (int64_t(1) << 31) || (int64_t)2 * T * I >= (int64_t(1) << 31) ||
+      (int64_t)2 * T * H >= (int64_t(1) << 31))
+    return W4A8_ERR_SHAPE;
+  if ((int64_t)E * 2 * I * (H / 8) >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
+  return W4A8_OK;
+}
+
+size_t gemm1_ws(int32_t T, int32_t H, bool bf16_x) { return bf16_x ? round_up((size_t)T * H, 256) : 0; }
+
+// gemm2's split-K partials: the same plan the launch uses.
+int gemm2_ksplit(int32_t T, int32_t H, int32_t I, int32_t E) {
+  if (!decode_fits(T)) return 1;
+  MoeGemmParams p{};
+  p.E = E; p.K = I; p.Nw = H; p.n_out = H; p.P = 2 * T;
+  plan_decode(p, false);
+  return p.ksplit;
+}
+
+size_t gemm2_ws(int32_t T, int32_t H, int32_t I, int32_t E) {
+  return round_up((size_t)gemm2_ksplit(T, H, I, E) * 2 * T * H * sizeof(float), 256);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* w4a8_status_str(int32_t status) {
+  switch (status) {
+    case W4A8_OK: return "ok";
+    case W4A8_ERR_NULL: return "a required pointer is NULL";
+    case W4A8_ERR_SHAPE: return "a size is out of range or breaks a divisibility rule";
+    case W4A8_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case W4A8_ERR_WORKSPACE: return "workspace too small";
+    case W4A8_ERR_UNSUPPORTED: return "unsupported configuration";
+    case W4A8_ERR_ARG: return "bad enum value or scale";
+    case W4A8_ERR_HIP: return "HIP runtime error at launch";
+    default: return "unknown status";
+  }
+}
+
+size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t I_or_K, int32_t E) {
+  switch (op) {
+    case W4A8_OP_ROUTE_SORT:
+      if (T_or_M < 0 || T_or_M > kMaxRouteTokens || E < 2 || E > W4A8_MAX_EXPERTS) return 0;
+      return round_up(route_workspace_bytes(T_or_M, E), 256);
+    case W4A8_OP_GEMM1:
+    case W4A8_OP_GEMM1_BF16:
+      if (check_moe_shape(T_or_M, H_or_N, I_or_K, E) != W4A8_OK) return 0;
+      return gemm1_ws(T_or_M, H_or_N, op == W4A8_OP_GEMM1_BF16);
+    case W4A8_OP_GEMM2:
+      if (check_moe_shape(T_or_M, H_or_N, I_or_K, E) != W4A8_OK) return 0;
+      return gemm2_ws(T_or_M, H_or_N, I_or_K, E);
+    case W4A8_OP_BLOCK_LINEAR:
+      return 0;
+    default:
+      return 0;
+  }
+}
+
+int32_t w4_pack(const uint16_t* w_bf16, int32_t E, int32_t N, int32_t K, int32_t* packed, float* scale,
+                void* stream) {
+  if (!w_bf16 || !packed || !scale) return W4A8_ERR_NULL;
+  if (E < 1 || N < 1 || K < 8 || K % 8 != 0) return W4A8_ERR_SHAPE;
+  if ((int64_t)E * N >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(packed) || !aligned16(scale)) return W4A8_ERR_ALIGN;
+  launch_w4_pack(w_bf16, (int64_t)E * N, K, packed, scale, as_stream(stream));
+  return launch_status();
+}
+
+int32_t fp8_quant_static(const uint16_t* x_bf16, int64_t n, float s, uint8_t* out, void* stream) {
+  if (n < 0) return W4A8_ERR_SHAPE;
+  if (!good_scale(s)) return W4A8_ERR_ARG;
+  if (n == 0) return W4A8_OK;
+  if (!x_bf16 || !out) return W4A8_ERR_NULL;
+  if (!aligned16(x_bf16) || !aligned16(out)) return W4A8_ERR_ALIGN;
+  launch_fp8_quant(x_bf16, n, s, out, as_stream(stream));
+  return launch_status();
+}
+
+int32_t moe_route_sort(const float* logits, int32_t T, int32_t E, int32_t* topk_ids, float* topk_w,
+                       int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws,
+                       size_t ws_bytes, void* stream) {
+  if (T < 0 || T > kMaxRouteTokens || E < 2 || E > W4A8_MAX_EXPERTS) return W4A8_ERR_SHAPE;
+  if (!counts || !offsets) return W4A8_ERR_NULL;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_pair || !pair_pos)) return W4A8_ERR_NULL;
+  if (!aligned16(counts) || !aligned16(offsets)) return W4A8_ERR_ALIGN;
+  if (T > 0 && (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(sorted_pair) ||
+                !aligned16(pair_pos)))
+    return W4A8_ERR_ALIGN;
+  const size_t need = w4a8_workspace_bytes(W4A8_OP_ROUTE_SORT, T, 0, 0, E);
+  if (ws_bytes < need) return W4A8_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W4A8_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return W4A8_ERR_ALIGN;
+  launch_route_sort(logits, T, E, topk_ids, topk_w, counts, offsets, sorted_pair, pair_pos, ws,
+                    as_stream(stream));
+  return launch_status();
+}
+
+int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x, const int32_t* w13, const float* s_w13,
+                       const int32_t* offsets, const int32_t* sorted_pair, int32_t T, int32_t H, int32_t I,
+                       int32_t E, int32_t act, float s_a, uint8_t* a_fp8, float* gateup_dbg, void* ws,
+                       size_t ws_bytes, void* stream) {
+  int32_t st = check_moe_shape(T, H, I, E);
+  if (st != W4A8_OK) return st;
+  if (x_dtype != W4A8_DT_BF16 && x_dtype != W4A8_DT_E4M3) return W4A8_ERR_ARG;
+  if (act != W4A8_ACT_SILU && act != W4A8_ACT_GELU_ERF && act != W4A8_ACT_GELU_TANH) return W4A8_ERR_ARG;
+  if (!good_scale(s_x) || !good_scale(s_a)) return W4A8_ERR_ARG;
+  if (T == 0) return W4A8_OK;
+  if (!x || !w13 || !s_w13 || !offsets || !sorted_pair || !a_fp8) return W4A8_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w13) || !aligned16(s_w13) || !aligned16(offsets) || !aligned16(sorted_pair) ||
+      !aligned16(a_fp8) || (gateup_dbg && !aligned16(gateup_dbg)))
+    return W4A8_ERR_ALIGN;
+  const bool bf16_x = x_dtype == W4A8_DT_BF16;
+  const size_t need = gemm1_ws(T, H, bf16_x);
+  if (ws_bytes < need) return W4A8_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W4A8_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return W4A8_ERR_ALIGN;
+  const bool decode = decode_fits(T);
+  if (!decode && !prefill_available()) return W4A8_ERR_UNSUPPORTED;
+
+  hipStream_t s = as_stream(stream);
+  const uint8_t* xq = static_cast<const uint8_t*>(x);
+  if (bf16_x) {
+    launch_fp8_quant(static_cast<const uint16_t*>(x), (int64_t)T * H, s_x, static_cast<uint8_t*>(ws), s);
+    xq = static_cast<const uint8_t*>(ws);
+  }
+  MoeGemmParams p{};
+  p.act = xq; p.w = w13; p.w_scale = s_w13; p.offsets = offsets; p.sorted_pair = sorted_pair;
+  p.E = E; p.K = H; p.Nw = 2 * I; p.n_out = I; p.P = 2 * T;
+  p.s_act = s_x; p.act_fn = act; p.s_a = s_a; p.a_out = a_fp8; p.dbg = gateup_dbg;
+  if (decode) {
+    plan_decode(p, true);
+    launch_moe_decode(p, true, s);
+  } else {
+    launch_moe_prefill(p, true, s);
+  }
+  return launch_status();
+}
+
+int32_t moe_gemm2_w4a8(const uint8_t* a_fp8, float s_a, const int32_t* w2, const float* s_w2,
+                       const int32_t* offsets, const int32_t* pair_pos, const float* topk_w, int32_t T,
+                       int32_t H, int32_t I, int32_t E, int32_t out_dtype, void* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int32_t st = check_moe_shape(T, H, I, E);
+  if (st != W4A8_OK) return st;
+  if (out_dtype != W4A8_DT_BF16 && out_dtype != W4A8_DT_F32) return W4A8_ERR_ARG;
+  if (!good_scale(s_a)) return W4A8_ERR_ARG;
+  if (T == 0) return W4A8_OK;
+  if (!a_fp8 || !w2 || !s_w2 || !offsets || !pair_pos || !topk_w || !out) return W4A8_ERR_NULL;
+  if (!aligned16(a_fp8) || !aligned16(w2) || !aligned16(s_w2) || !aligned16(offsets) || !aligned16(pair_pos) ||
+      !aligned16(topk_w) || !aligned16(out))
+    return W4A8_ERR_ALIGN;
+  const size_t need = gemm2_ws(T, H, I, E);
+  if (ws_bytes < need) return W4A8_ERR_WORKSPACE;
+  if (!ws) return W4A8_ERR_NULL;
+  if (!aligned16(ws)) return W4A8_ERR_ALIGN;
+  const bool decode = decode_fits(T);
+  if (!decode && !prefill_available()) return W4A8_ERR_UNSUPPORTED;
+
+  hipStream_t s = as_stream(stream);
+  MoeGemmParams p{};
+  p.act = a_fp8; p.w = w2; p.w_scale = s_w2; p.offsets = offsets; p.sorted_pair = nullptr;
+  p.E = E; p.K = I; p.Nw = H; p.n_out = H; p.P = 2 * T;
+  p.s_act = s_a; p.partial = static_cast<float*>(ws);
+  int ksplit = 1;
+  if (decode) {
+    plan_decode(p, false);
+    ksplit = p.ksplit;
+    launch_moe_decode(p, false, s);
+  } else {
+    launch_moe_prefill(p, false, s);
+  }
+  if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;
+  launch_combine(p.partial, ksplit, 2 * T, H, pair_pos, topk_w, T, out_dtype == W4A8_DT_BF16, out, s);
+  return launch_status();
+}
+
+int32_t fp8_block_quant(const uint16_t* w_bf16, int32_t N, int32_t K, uint8_t* w_e4m3, float* scales,
+                        void* stream) {
+  if (!w_bf16 || !w_e4m3 || !scales) return W4A8_ERR_NULL;
+  if (N < 1 || K < 16 || K % 16 != 0 || (int64_t)N * K >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
+  if ((N + 127) / 128 > 65535) return W4A8_ERR_SHAPE;
+  if (!aligned16(w_bf16) || !aligned16(w_e4m3) || !aligned16(scales)) return W4A8_ERR_ALIGN;
+  launch_fp8_block_quant(w_bf16, N, K, w_e4m3, scales, as_stream(stream));
+  return launch_status();
+}
+
+int32_t fp8_block_linear(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float* s, int32_t M, int32_t N,
+                         int32_t K, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws; (void)ws_bytes;
+  if (!x_bf16 || !w_e4m3 || !s || !y_bf16) return W4A8_ERR_NULL;
+  if (M < 1 || M > 16 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return W4A8_ERR_SHAPE;
+  if ((int64_t)N * K >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
+  if ((int64_t)M * K * 2 > 65536) return W4A8_ERR_UNSUPPORTED;   // activation rows staged in 64 KB of LDS
+  if (!aligned16(x_bf16) || !aligned16(w_e4m3) || !aligned16(s) || !aligned16(y_bf16)) return W4A8_ERR_ALIGN;
+  launch_fp8_block_linear(x_bf16, w_e4m3, s, M, N, K, y_bf16, as_stream(stream));
+  return launch_status();
+}
+
+}  // extern "C"

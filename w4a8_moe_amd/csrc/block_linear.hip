@@ -1,0 +1,112 @@
+// Block-FP8 weight-only decode GEMV / small-M GEMM (the FP8_PB_WO projections of the
+// page "qwen4_exp: serve the block-FP8 dense projections natively (+25% decode)":
+// e4m3 weight [N,K] and one fp32 scale per 128x128 block; the activation stays bf16).
+//
+//   y[m][n] = bf16( sum_kb S[n/128][kb] * sum_{k in kb} x[m][k] * dec(W[n][k]) )
+//
+// The contraction runs on the bf16 MFMA: an E4M3 value is exact in bf16 (3 mantissa
+// bits, exponents 2^-9..2^8), so each weight byte is widened in registers
+// (v_cvt_pk_f32_fp8, then the upper halves of two fp32 are packed into one dword) and
+// multiplied against the bf16 activations with fp32 accumulation. Each 128-column block
+// is accumulated on its own and added to the running sum with its scale.
+//
+// Mapping: a workgroup of 4 waves covers 64 output rows, one 16-row block per wave, all
+// of K. The M <= 16 activation rows are staged once per workgroup in LDS, compactly
+// (no padding columns). Weight loads are 2 x 16 B per lane per 128-K block.
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a8 {
+
+constexpr int kBlWaves = 4;
+constexpr int kBlDepth = 4;     // 128-K blocks of weights in flight per wave
+
+// 4 E4M3 codes -> 4 bf16 values in two dwords (exact).
+__device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t c, uint32_t& lo, uint32_t& hi) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  const v2f a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+  const v2f b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+  lo = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+  hi = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+}
+
+__device__ __forceinline__ v8bf bf16_operand(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+  v4i t = {(int)d0, (int)d1, (int)d2, (int)d3};
+  return __builtin_bit_cast(v8bf, t);
+}
+
+__global__ __launch_bounds__(kBlWaves * kWave) void fp8_block_linear_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, const float* __restrict__ S,
+    int M, int N, int K, uint16_t* __restrict__ y) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int KB = K >> 7;
+  // ---- stage x: unit (kb, j, g, m) = 8 bf16 = x[m][kb*128 + g*32 + j*8 .. +8], stored at
+  //      ((kb*4 + j)*4 + g)*M + m, so lane (m, g) of MFMA j reads 16 contiguous bytes.
+  const int units = M * (K >> 3);
+  for (int u = tid; u < units; u += kBlWaves * kWave) {
+    const int m = u / (K >> 3), c8 = u - m * (K >> 3);       // 8-element chunk of row m
+    const int kb = c8 >> 4, within = c8 & 15;                // 16 chunks per 128-K block
+    const int g = within >> 2, j = within & 3;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + c8 * 8);
+    *reinterpret_cast<uint4*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 4)) = v;
+  }
+  __syncthreads();
+  const int rb = blockIdx.x * kBlWaves + wave;               // 16-row block
+  if (rb * 16 >= N) return;
+  const int i = lane & 15, g = lane >> 4;
+  const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
+  const float* srow = S + (size_t)((rb * 16) >> 7) * KB;
+  const bool col_ok = i < M;
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  uint4 q0[kBlDepth], q1[kBlDepth];
+#pragma unroll
+  for (int d = 0; d < kBlDepth; ++d)
+    if (d < KB) { q0[d] = *reinterpret_cast<const uint4*>(wp + d * 128); q1[d] = *reinterpret_cast<const uint4*>(wp + d * 128 + 16); }
+  for (int kb0 = 0; kb0 < KB; kb0 += kBlDepth) {
+#pragma unroll
+    for (int d = 0; d < kBlDepth; ++d) {
+      const int kb = kb0 + d;
+      if (kb < KB) {
+        const uint4 a0 = q0[d], a1 = q1[d];
+        if (kb + kBlDepth < KB) {
+          q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128);
+          q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128 + 16);
+        }
+        const uint32_t c[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        v4f blk = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                        // MFMA j: bytes 8j..8j+7 of the lane's 32
+          uint32_t d0, d1, d2, d3;
+          e4m3x4_to_bf16x4(c[2 * j], d0, d1);
+          e4m3x4_to_bf16x4(c[2 * j + 1], d2, d3);
+          const v8bf a = bf16_operand(d0, d1, d2, d3);
+          uint4 bv = make_uint4(0, 0, 0, 0);
+          if (col_ok) bv = *reinterpret_cast<const uint4*>(lds + ((((kb * 4 + j) * 4 + g) * M + i) << 4));
+          const v8bf b = bf16_operand(bv.x, bv.y, bv.z, bv.w);
+          blk = mfma_bf16_16x16x32(a, b, blk);
+        }
+        const float sc = srow[kb];
+        acc[0] += sc * blk[0]; acc[1] += sc * blk[1]; acc[2] += sc * blk[2]; acc[3] += sc * blk[3];
+      }
+    }
+  }
+  // lane holds rows rb*16 + 4g + v of column (token) i
+  if (!col_ok) return;
+  const int n = rb * 16 + 4 * g;
+  uint2 o;
+  o.x = f32_to_bf16_bits(acc[0]) | f32_to_bf16_bits(acc[1]) << 16;
+  o.y = f32_to_bf16_bits(acc[2]) | f32_to_bf16_bits(acc[3]) << 16;
+  *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
+}
+
+void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K,
+                             uint16_t* y, hipStream_t st) {
+  const int rows_per_wg = kBlWaves * 16;
+  const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
+  const size_t lds = (size_t)M * K * sizeof(uint16_t);
+  hipLaunchKernelGGL(fp8_block_linear_kernel, dim3(grid), dim3(kBlWaves * kWave), lds, st, x, w, s, M, N, K, y);
+}
+
+}  // namespace w4a8

@@ -1,0 +1,66 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+// ---- quant.hip
+void launch_w4_pack(const uint16_t* w, int64_t rows, int K, int32_t* packed, float* scale, hipStream_t st);
+void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st);
+void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st);
+
+// ---- route.hip
+size_t route_workspace_bytes(int T, int E);
+void launch_route_sort(const float* logits, int T, int E, int32_t* ids, float* tw, int32_t* counts,
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st);
+
+// ---- moe_decode.hip / moe_prefill.hip: grouped GEMM of the routed experts
+// One description serves both GEMMs:
+//   gate|up (gemm1): rows of the activation are tokens gathered through sorted_pair,
+//     K = H, weight rows Nw = 2I, output channels n_out = I (gate row n pairs with up
+//     row I + n), fused activation + fp8 requant into a_out, optional fp32 dbg.
+//   down (gemm2):    rows are the sorted rows themselves, K = I, Nw = n_out = H,
+//     fp32 output Y (scaled) into partial[slice][P][H].
+struct MoeGemmParams {
+  const uint8_t* act;          // E4M3 activation rows, [rows][K]
+  const int32_t* w;            // packed int4 [E][Nw][K/8]
+  const float* w_scale;        // [E][Nw]
+  const int32_t* offsets;      // [E+1]
+  const int32_t* sorted_pair;  // [P] (gate|up only)
+  int E, K, Nw, n_out, P;
+  float s_act;                 // static scale of the activation rows
+  // gate|up epilogue
+  int act_fn;
+  float s_a;
+  uint8_t* a_out;              // [P][I]
+  float* dbg;                  // [P][2I] or nullptr
+  // down epilogue
+  float* partial;              // [ksplit][P][H]
+  // decode launch shape (set by plan_decode)
+  int kslice, ksplit, groups, lds_bytes, max_tiles;
+};
+
+constexpr int kDecodeWaves = 8;      // waves per workgroup of the streaming kernel
+constexpr int kDecodeMaxTiles = 4;   // 16-row column tiles per expert (64 rows)
+constexpr int kDecodeLds = 64 * 1024;
+
+bool decode_fits(int T);             // the streaming kernel handles T tokens
+void plan_decode(MoeGemmParams& p, bool gateup);
+void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st);
+
+bool prefill_available();
+size_t prefill_gemm2_partial_bytes(int T, int H);
+void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st);
+
+// combine: out[t] = w0 * sum_s partial[s][pair_pos[2t]] + w1 * sum_s partial[s][pair_pos[2t+1]]
+void launch_combine(const float* partial, int ksplit, int P, int H, const int32_t* pair_pos,
+                    const float* topk_w, int T, bool out_bf16, void* out, hipStream_t st);
+
+// ---- block_linear.hip
+void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K,
+                             uint16_t* y, hipStream_t st);
+
+}  // namespace w4a8

@@ -1,0 +1,149 @@
+// Load-time and elementwise quantization kernels:
+//  * w4_pack: column-wise symmetric int4 quantization + reorder packing into int32
+//    (int4_experts {bits 4, sym, group column} and pack_method reorder in the
+//    quantization_config of the page "ROCm: enable trillion-parameter MoE models with
+//    INT4-FP8 single node"; column-wise INT4 quantization and INT4-into-INT32 packing
+//    in the Highlights of "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm").
+//  * fp8_quant_static: tensor-wise static E4M3 quantization (same Highlights;
+//    activation_scheme static).
+//  * fp8_block_quant: 128x128 block-scaled E4M3 weights (FP8_PB_WO layout of the page
+//    "qwen4_exp: serve the block-FP8 dense projections natively (+25% decode)").
+// All quotients are formed with the correctly rounded fp32 division (the library is
+// built without fast-math), then rounded to nearest even.
+#include "common.h"
+#include "kernels.h"
+
+namespace w4a8 {
+
+// ---------------------------------------------------------------------------- w4_pack
+// One 256-thread workgroup per weight row. Pass 1 reduces max|w| (bf16 magnitudes
+// compare as integers), pass 2 re-reads the row (an L2 hit) and writes one int32 per
+// 8 elements. Loads are 16 B per lane, stores 4 B per lane, both contiguous per wave.
+constexpr int kPackThreads = 256;
+
+__device__ __forceinline__ uint32_t quant_nibble(uint32_t bits, float s) {
+  float q = __builtin_rintf(bf16_bits_to_f32(bits) / s);
+  q = __builtin_fminf(__builtin_fmaxf(q, -8.0f), 7.0f);
+  return (uint32_t)((int)q) & 0xFu;
+}
+
+__global__ __launch_bounds__(kPackThreads) void w4_pack_kernel(
+    const uint16_t* __restrict__ w, int K, int32_t* __restrict__ packed, float* __restrict__ scale) {
+  const size_t row = blockIdx.x;
+  const int G = K >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(w + row * (size_t)K);
+  uint32_t amax = 0;
+  for (int j = threadIdx.x; j < G; j += kPackThreads) {
+    uint4 v = src[j];
+    uint32_t m = max(max(max(v.x & 0x7FFFu, v.x >> 16 & 0x7FFFu), max(v.y & 0x7FFFu, v.y >> 16 & 0x7FFFu)),
+                     max(max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu)));
+    amax = max(amax, m);
+  }
+  // workgroup max: wave reduction, then across the 4 waves through LDS
+  for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+  __shared__ uint32_t red[kPackThreads / kWave];
+  if (lane_id() == 0) red[wave_id()] = amax;
+  __syncthreads();
+  amax = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = bf16_bits_to_f32(amax) / 7.0f;
+  if (threadIdx.x == 0) scale[row] = s;
+  int32_t* dst = packed + row * (size_t)G;
+  for (int j = threadIdx.x; j < G; j += kPackThreads) {
+    uint32_t word = 0;
+    if (s != 0.0f) {
+      uint4 v = src[j];
+      // element e of the group: e = 0..7 at bf16 slot e of the 16-byte load
+      const uint32_t e0 = v.x & 0xFFFFu, e1 = v.x >> 16, e2 = v.y & 0xFFFFu, e3 = v.y >> 16;
+      const uint32_t e4 = v.z & 0xFFFFu, e5 = v.z >> 16, e6 = v.w & 0xFFFFu, e7 = v.w >> 16;
+      // reorder layout: byte b = element b (low nibble) | element 4+b (high nibble)
+      word = quant_nibble(e0, s) | quant_nibble(e4, s) << 4 |
+             quant_nibble(e1, s) << 8 | quant_nibble(e5, s) << 12 |
+             quant_nibble(e2, s) << 16 | quant_nibble(e6, s) << 20 |
+             quant_nibble(e3, s) << 24 | quant_nibble(e7, s) << 28;
+    }
+    dst[j] = (int32_t)word;
+  }
+}
+
+void launch_w4_pack(const uint16_t* w, int64_t rows, int K, int32_t* packed, float* scale, hipStream_t st) {
+  // rows <= E * N < 2^31 is checked by the caller
+  hipLaunchKernelGGL(w4_pack_kernel, dim3((unsigned)rows), dim3(kPackThreads), 0, st, w, K, packed, scale);
+}
+
+// -------------------------------------------------------------------- fp8_quant_static
+// 8 elements per thread per iteration (16 B in, 8 B out); a grid-stride loop.
+__device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s) {
+  return pack4_e4m3(bf16_bits_to_f32(lo & 0xFFFFu) / s, bf16_bits_to_f32(lo >> 16) / s,
+                    bf16_bits_to_f32(hi & 0xFFFFu) / s, bf16_bits_to_f32(hi >> 16) / s);
+}
+
+__global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restrict__ x, int64_t n, float s,
+                                                        uint8_t* __restrict__ out) {
+  const int64_t n8 = n >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(x);
+  uint2* dst = reinterpret_cast<uint2*>(out);
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
+    uint4 v = src[i];
+    dst[i] = make_uint2(quant4(v.x, v.y, s), quant4(v.z, v.w, s));
+  }
+  // tail (n % 8 elements): one thread each
+  const int64_t t = n8 * 8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  if (t < n && t < n8 * 8 + 8) {
+    uint32_t c = pack4_e4m3(bf16_bits_to_f32(x[t]) / s, 0.f, 0.f, 0.f);
+    out[t] = (uint8_t)(c & 0xFFu);
+  }
+}
+
+void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st) {
+  const int64_t n8 = n >> 3;
+  int64_t blocks = (n8 + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(fp8_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, s, out);
+}
+
+// ---------------------------------------------------------------- fp8_block_quant
+// One 256-thread workgroup per 128x128 block: thread -> (row = tid / 2, 64-column half).
+__global__ __launch_bounds__(256) void fp8_block_quant_kernel(const uint16_t* __restrict__ w, int N, int K,
+                                                              uint8_t* __restrict__ q, float* __restrict__ S) {
+  const int nb = blockIdx.y, kb = blockIdx.x, KB = gridDim.x;
+  const int r = nb * 128 + (threadIdx.x >> 1);
+  const int c0 = kb * 128 + (threadIdx.x & 1) * 64;
+  const bool row_ok = r < N;
+  uint4 v[8];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c0 + 8 * i;
+    if (row_ok && c < K) {
+      v[i] = *reinterpret_cast<const uint4*>(w + (size_t)r * K + c);
+      amax = max(amax, max(max(max(v[i].x & 0x7FFFu, v[i].x >> 16 & 0x7FFFu), max(v[i].y & 0x7FFFu, v[i].y >> 16 & 0x7FFFu)),
+                           max(max(v[i].z & 0x7FFFu, v[i].z >> 16 & 0x7FFFu), max(v[i].w & 0x7FFFu, v[i].w >> 16 & 0x7FFFu))));
+    } else {
+      v[i] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+  __shared__ uint32_t red[4];
+  if (lane_id() == 0) red[wave_id()] = amax;
+  __syncthreads();
+  amax = max(max(red[0], red[1]), max(red[2], red[3]));
+  const float s = bf16_bits_to_f32(amax) / 448.0f;
+  if (threadIdx.x == 0) S[(size_t)nb * KB + kb] = s;
+  if (!row_ok) return;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = c0 + 8 * i;
+    if (c >= K) break;
+    uint2 o = make_uint2(0, 0);
+    if (s != 0.0f) o = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+    *reinterpret_cast<uint2*>(q + (size_t)r * K + c) = o;
+  }
+}
+
+void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st) {
+  dim3 grid((K + 127) / 128, (N + 127) / 128);
+  hipLaunchKernelGGL(fp8_block_quant_kernel, grid, dim3(256), 0, st, w, N, K, q, S);
+}
+
+}  // namespace w4a8
