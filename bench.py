@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_decode", choices=sorted(synth.MOE_CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-gemv", action="store_true", help="skip timing the block-FP8 GEMVs")
+    ap.add_argument("--copy-ref", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
 
 
@@ -48,6 +50,20 @@ def static_scales(name):
 
 def bf16_dev(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+def counter_traffic(workload):
+    """HBM bytes per gate|up launch from the committed rocprofv3 counters, or None when
+    they were taken on another workload or on a different kernel source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"moe_decode_{workload.replace('_decode', '')}_T32.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    src = open(os.path.join(ROOT, d["source"]), "rb").read()
+    if d.get("workload") != workload or hashlib.sha256(src).hexdigest() != d["source_sha256"]:
+        return None
+    return int(d["traffic_bytes_per_launch"])
 
 
 def moe_bytes(cfg, counts):
@@ -246,10 +262,17 @@ def main():
         "calls_us": {k: round(v, 2) for k, v in per_call.items()},
         "roofline": {"kernel": "moe_gemm1_w4a8 (moe_decode_kernel<gate|up>)", "bound": "hbm",
                      "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(cfg.name),
                      "bytes_per_launch": int(gemm1_bytes)},
         "w4_pack": {"ms": round(pack_ms, 3), "GB/s": round(pack_bytes / pack_ms / 1e6, 1)},
     }
+    if args.copy_ref:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        result["copy_ref_bytes"] = 1 << 30
     if not args.no_block_gemv:
         result["block_fp8_gemv"] = bench_block_gemv(torch, W, dev)
     if not args.no_cpu_baseline:

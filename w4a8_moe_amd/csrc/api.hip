@@ -33,6 +33,7 @@ int32_t check_moe_shape(int32_t T, int32_t H, int32_t I, int32_t E) {
       (int64_t)2 * T * H >= (int64_t(1) << 31))
     return W4A8_ERR_SHAPE;
   if ((int64_t)E * 2 * I * (H / 8) >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
+  if ((int64_t)I * H >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;   // one expert's packed matrix < 2 GiB
   return W4A8_OK;
 }
 

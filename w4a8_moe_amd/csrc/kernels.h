@@ -43,9 +43,15 @@ struct MoeGemmParams {
   int kslice, ksplit, groups, lds_bytes, max_tiles;
 };
 
-constexpr int kDecodeWaves = 8;      // waves per workgroup of the streaming kernel
-constexpr int kDecodeMaxTiles = 4;   // 16-row column tiles per expert (64 rows)
-constexpr int kDecodeLds = 64 * 1024;
+#ifndef W4A8_DECODE_WAVES
+#define W4A8_DECODE_WAVES 8
+#endif
+#ifndef W4A8_DECODE_LDS_KB
+#define W4A8_DECODE_LDS_KB 64
+#endif
+constexpr int kDecodeWaves = W4A8_DECODE_WAVES;   // waves per workgroup of the streaming kernel
+constexpr int kDecodeMaxTiles = 4;                // 16-row column tiles per expert (64 rows)
+constexpr int kDecodeLds = W4A8_DECODE_LDS_KB * 1024;
 
 bool decode_fits(int T);             // the streaming kernel handles T tokens
 void plan_decode(MoeGemmParams& p, bool gateup);

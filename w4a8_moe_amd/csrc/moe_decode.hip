@@ -26,12 +26,13 @@
 // subtraction, so only fp32 rounding is left.
 //
 // Mapping. A workgroup = 8 waves on one expert and one K-slice. The activation rows of
-// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS as
-// fp16, in the order the MFMA B operand is read (one ds_read_b128 per lane covers 1 KB
-// per wave without bank conflicts). Each wave owns two blocks of 16 weight rows (gate
-// rows n..n+15 and up rows I+n..I+n+15, or two blocks of down rows) and streams them
-// with 16-byte loads, prefetched kDepth k-steps (of 128) ahead; one load instruction of
-// a wave covers 64 contiguous bytes of 16 rows.
+// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS as E4M3
+// codes, in the order the MFMA B operand is read (one ds_read_b64 per lane, 512 bytes
+// per wave without bank conflicts), and widened to fp16 as they are read. Each wave owns
+// two blocks of 16 weight rows (gate rows n..n+15 and up rows I+n..I+n+15, or two blocks
+// of down rows) and streams them with 16-byte buffer loads, kDepth k-steps (of 128)
+// ahead, without a break at LDS chunk boundaries; one load instruction of a wave covers
+// 64 contiguous bytes of 16 rows.
 #include <algorithm>
 
 #include "common.h"
@@ -39,7 +40,24 @@
 
 namespace w4a8 {
 
-constexpr int kDepth = 4;          // k-steps of weights in flight per wave
+// Tuning knobs (defaults chosen by measurement on MI355X):
+//   W4A8_DECODE_DEPTH     k-steps of weights in flight per wave (LDS chunks hold multiples)
+//   W4A8_DECODE_NT_LOADS  stream the weights with the nontemporal hint (measured slower)
+//   W4A8_DECODE_BODY      k-steps per unrolled loop body
+#ifndef W4A8_DECODE_DEPTH
+#define W4A8_DECODE_DEPTH 4
+#endif
+#ifndef W4A8_DECODE_NT_LOADS
+#define W4A8_DECODE_NT_LOADS 0
+#endif
+#ifndef W4A8_DECODE_BODY
+#define W4A8_DECODE_BODY 16
+#endif
+constexpr int kDepth = W4A8_DECODE_DEPTH;
+constexpr int kBody = W4A8_DECODE_BODY;                    // k-steps per unrolled loop body
+constexpr int kStageBatch = 8;                             // staging units in flight per thread
+static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
+constexpr int kWeightLoadAux = W4A8_DECODE_NT_LOADS ? 2 : 0;   // cache-policy bits: nt
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
 __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -52,9 +70,8 @@ __device__ __forceinline__ uint32_t cvt2_e4m3_f16(uint32_t codes) {
 
 // One packed word (8 int4 codes, reorder layout) -> 8 fp16 values (q + 8) * 2^-9 in K order.
 __device__ __forceinline__ v8h int4x8_to_f16_offset(uint32_t w) {
-  const uint32_t y = w ^ 0x88888888u;
-  const uint32_t lo = y & 0x0F0F0F0Fu;            // codes of elements 0..3
-  const uint32_t hi = (y >> 4) & 0x0F0F0F0Fu;     // codes of elements 4..7
+  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // codes of elements 0..3
+  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // codes of elements 4..7
   v4i r = {(int)cvt2_e4m3_f16<false>(lo), (int)cvt2_e4m3_f16<true>(lo),
            (int)cvt2_e4m3_f16<false>(hi), (int)cvt2_e4m3_f16<true>(hi)};
   return __builtin_bit_cast(v8h, r);
@@ -68,10 +85,64 @@ __device__ __forceinline__ uint32_t word_of(const uint4& q, int m) {
   return m == 0 ? q.x : (m == 1 ? q.y : (m == 2 ? q.z : q.w));
 }
 
+// Raw buffer loads: an offset at or past the resource's size returns zeros and moves no
+// data, so the weight stream below issues the same loads every step (no branches around
+// loads, which would make the compiler drain every outstanding load before each use).
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kWeightLoadAux));
+}
+
+// Barrier for LDS hand-off only: waits for this wave's LDS operations, not for its
+// outstanding global loads (the weight prefetch stays in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// One k-step (128 K) of one wave: 4 MFMAs of K = 32 per weight block and column tile,
+// plus the offset correction, B read from the fp16 LDS chunk.
+template <int MAXT>
+__device__ __forceinline__ void mma_step(const uint4& a0, const uint4& a1, const uint8_t* lds, int s, int S, int nt,
+                                         int lane, const v8h& corr_op, v4f* acc0, v4f* acc1, v4f* corr) {
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const v8h A0 = int4x8_to_f16_offset(word_of(a0, m));
+    const v8h A1 = int4x8_to_f16_offset(word_of(a1, m));
+#pragma unroll
+    for (int j = 0; j < MAXT; ++j) {
+      if (j < nt) {
+        const v8h b = __builtin_bit_cast(
+            v8h, *reinterpret_cast<const uint4*>(lds + ((j * S + s) * 4 + m) * 1024 + lane * 16));
+        acc0[j] = mfma_f16(A0, b, acc0[j]);
+        acc1[j] = mfma_f16(A1, b, acc1[j]);
+        corr[j] = mfma_f16(corr_op, b, corr[j]);
+      }
+    }
+  }
+}
+
+// Consume one k-step from the register ring, then refill the same registers with the
+// k-step kDepth ahead (out-of-range offsets past this wave's K-range move no data).
+template <int MAXT>
+__device__ __forceinline__ void stream_step(uint4& q0, uint4& q1, __amdgpu_buffer_rsrc_t wr, uint32_t off0,
+                                            uint32_t off1, int ST, int ST1, int gstep, const uint8_t* lds, int s,
+                                            int S, int nt, int lane, const v8h& corr_op, v4f* acc0, v4f* acc1,
+                                            v4f* corr) {
+  mma_step<MAXT>(q0, q1, lds, s, S, nt, lane, corr_op, acc0, acc1, corr);
+  __builtin_amdgcn_sched_barrier(0);                        // keep the refill after the use
+  const int nxt = gstep + kDepth;
+  q0 = buf_ld16(wr, nxt < ST ? off0 + nxt * 64 : kOutOfRange);
+  q1 = buf_ld16(wr, nxt < ST1 ? off1 + nxt * 64 : kOutOfRange);
+}
+
 template <bool GATEUP, int MAXT>
 __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int tid = threadIdx.x, lane = lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(wave_id());   // wave-uniform (scalar) index
   int bid = blockIdx.x;
   const int group = bid % p.groups; bid /= p.groups;
   const int slice = bid % p.ksplit;
@@ -82,7 +153,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const int nt = min((cnt + 15) >> 4, MAXT);
   const int k_begin = slice * p.kslice;
   const int k_end = min(p.K, k_begin + p.kslice);
-  const int kc_max = ((p.lds_bytes / (32 * nt)) / 128) * 128;   // fp16 rows of 16*nt tokens
+  const int kc_max = ((p.lds_bytes / (32 * nt)) / (128 * kDepth)) * (128 * kDepth);   // fp16 rows of 16*nt tokens
 
   // weight row blocks of this wave: gate|up -> (cb, n_out/16 + cb); down -> (2cb, 2cb + 1)
   const int cb = group * kDecodeWaves + wave;
@@ -91,10 +162,14 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const bool has_work = blk0 * 16 < (GATEUP ? p.n_out : p.Nw);
   const bool has1 = GATEUP || blk1 * 16 < p.Nw;
   const int i = lane & 15, g = lane >> 4;
-  const size_t row_bytes = (size_t)p.K / 2;
-  const uint8_t* wbase = reinterpret_cast<const uint8_t*>(p.w) + (size_t)e * p.Nw * row_bytes + g * 16;
-  const uint8_t* w0_ptr = wbase + (size_t)(blk0 * 16 + i) * row_bytes;
-  const uint8_t* w1_ptr = wbase + (size_t)((has1 ? blk1 : blk0) * 16 + i) * row_bytes;
+  const uint32_t row_bytes = (uint32_t)p.K / 2;
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(reinterpret_cast<const uint8_t*>(p.w) + (size_t)e * p.Nw * row_bytes), (short)0,
+      (int)(p.Nw * row_bytes), 0x00020000);
+  const uint32_t off0 = (uint32_t)(blk0 * 16 + i) * row_bytes + g * 16 + k_begin / 2;
+  const uint32_t off1 = (uint32_t)((has1 ? blk1 : blk0) * 16 + i) * row_bytes + g * 16 + k_begin / 2;
+  const int ST = has_work ? (k_end - k_begin) >> 7 : 0;    // k-steps of 128 this wave streams
+  const int ST1 = has1 ? ST : 0;
 
   v4f acc0[MAXT], acc1[MAXT], corr[MAXT];
 #pragma unroll
@@ -105,72 +180,82 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
 #pragma unroll
   for (int r = 0; r < 8; ++r) corr_op[r] = (_Float16)(-8.0f / 512.0f);
 
+  // prefetch the first kDepth k-steps; the stream runs on across chunk boundaries
+  uint4 q0[kDepth], q1[kDepth];
+#pragma unroll
+  for (int d = 0; d < kDepth; ++d) {
+    q0[d] = buf_ld16(wr, d < ST ? off0 + d * 64 : kOutOfRange);
+    q1[d] = buf_ld16(wr, d < ST1 ? off1 + d * 64 : kOutOfRange);
+  }
+  int sg = 0;                                               // k-steps consumed so far
   for (int kc0 = k_begin; kc0 < k_end; kc0 += kc_max) {
     const int klen = min(kc_max, k_end - kc0);
-    const int S = klen >> 7;                                // k-steps of 128 in this chunk
-    if (kc0 != k_begin) __syncthreads();                    // LDS reuse
-    // ---- stage the activation rows of this chunk as fp16. Unit = 8 codes of one row:
-    //      (tile j, k-step s, sub-step m, lane c + 16 g) -> 16 bytes at
+    const int S = klen >> 7;                                // k-steps in this chunk
+    if (kc0 != k_begin) lds_barrier();                      // LDS reuse
+    // ---- stage the activation rows of this chunk, widened to fp16 once. Unit = 8 codes of
+    //      one row: (tile j, k-step s, sub-step m, lane c + 16 g) -> 16 bytes at
     //      ((j*S + s)*4 + m)*1024 + lane*16, so MFMA m of k-step s reads one b128 per lane.
     {
-      const int R = klen >> 3;                              // 8-code units per row
-      const int units = nt * 16 * R;
-      for (int u = tid; u < units; u += kDecodeWaves * kWave) {
-        const int col = u / R, kk = u - col * R;
-        const int j = col >> 4, c = col & 15;
-        const int s = kk >> 4, gg = (kk >> 2) & 3, m = kk & 3;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (col < cnt) {
-          const int src_row = GATEUP ? (p.sorted_pair[seg0 + col] >> 1) : (seg0 + col);
-          const uint2 q = *reinterpret_cast<const uint2*>(p.act + (size_t)src_row * p.K + kc0 + kk * 8);
-          v = make_uint4(cvt2_e4m3_f16<false>(q.x), cvt2_e4m3_f16<true>(q.x),
-                         cvt2_e4m3_f16<false>(q.y), cvt2_e4m3_f16<true>(q.y));
+      // Threads walk the LDS slots in order (16 bytes each, consecutive threads write
+      // consecutive slots: no bank conflicts); slot v of the chunk is
+      // (tile j, k-step st, sub-step m) = v / 64 and lane (c + 16 gg) = v % 64, which holds
+      // codes 8 * (st*16 + gg*4 + m) .. +8 of token column j*16 + c. Batches of kStageBatch
+      // slots per thread issue all their global loads before waiting on the first.
+      const int slots = nt * S * 4 * 64;
+      for (int v0 = 0; v0 < slots; v0 += kStageBatch * kDecodeWaves * kWave) {
+        int src[kStageBatch], kk[kStageBatch];
+#pragma unroll
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int v = v0 + b * kDecodeWaves * kWave + tid;
+          const int blk = v >> 6, l = v & 63;
+          const int m = blk & 3, js = blk >> 2;
+          const int j = js / S, st = js - j * S;
+          const int col = j * 16 + (l & 15);
+          kk[b] = st * 16 + (l >> 4) * 4 + m;
+          src[b] = (v < slots && col < cnt) ? (GATEUP ? (p.sorted_pair[seg0 + col] >> 1) : (seg0 + col)) : -1;
         }
-        *reinterpret_cast<uint4*>(lds + ((j * S + s) * 4 + m) * 1024 + (c + 16 * gg) * 16) = v;
-      }
-    }
-    __syncthreads();
-    if (!has_work) continue;
-    // ---- stream the weights of this chunk
-    const uint8_t* p0 = w0_ptr + kc0 / 2;
-    const uint8_t* p1 = w1_ptr + kc0 / 2;
-    uint4 q0[kDepth], q1[kDepth];
+        uint2 q[kStageBatch];
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d) {
-      if (d < S) {
-        q0[d] = ld16(p0 + d * 64);
-        if (has1) q1[d] = ld16(p1 + d * 64);
-      }
-    }
-    for (int s0 = 0; s0 < S; s0 += kDepth) {
+        for (int b = 0; b < kStageBatch; ++b)
+          q[b] = src[b] >= 0 ? *reinterpret_cast<const uint2*>(p.act + (size_t)src[b] * p.K + kc0 + kk[b] * 8)
+                             : make_uint2(0, 0);
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        const int s = s0 + d;
-        if (s < S) {
-          const uint4 a0 = q0[d];
-          const uint4 a1 = has1 ? q1[d] : a0;
-          if (s + kDepth < S) {
-            q0[d] = ld16(p0 + (s + kDepth) * 64);
-            if (has1) q1[d] = ld16(p1 + (s + kDepth) * 64);
-          }
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {                     // 4 MFMAs of K = 32
-            const v8h A0 = int4x8_to_f16_offset(word_of(a0, m));
-            const v8h A1 = int4x8_to_f16_offset(word_of(a1, m));
-#pragma unroll
-            for (int j = 0; j < MAXT; ++j) {
-              if (j < nt) {
-                const v8h b = __builtin_bit_cast(
-                    v8h, *reinterpret_cast<const uint4*>(lds + ((j * S + s) * 4 + m) * 1024 + lane * 16));
-                acc0[j] = mfma_f16(A0, b, acc0[j]);
-                acc1[j] = mfma_f16(A1, b, acc1[j]);
-                corr[j] = mfma_f16(corr_op, b, corr[j]);
-              }
-            }
-          }
+        for (int b = 0; b < kStageBatch; ++b) {
+          const int v = v0 + b * kDecodeWaves * kWave + tid;
+          if (v >= slots) break;
+          const uint4 w = make_uint4(cvt2_e4m3_f16<false>(q[b].x), cvt2_e4m3_f16<true>(q[b].x),
+                                     cvt2_e4m3_f16<false>(q[b].y), cvt2_e4m3_f16<true>(q[b].y));
+          *reinterpret_cast<uint4*>(lds + (size_t)v * 16) = w;
         }
       }
     }
+    lds_barrier();
+    // ---- stream the weights of this chunk: full rounds of kDepth k-steps issue a load
+    //      for every step they consume (no branch around any load); only the last chunk
+    //      can end with a partial round, which issues no loads
+    if (has_work) {
+      // The compiler drains all outstanding loads at every loop header, so the k-steps run
+      // in unrolled bodies of kBody steps (precise waits inside), then in rounds of kDepth.
+      constexpr int body = MAXT <= 2 ? kBody : kDepth;     // keep 4-tile code within registers
+      int s = 0;
+      for (; s + body <= S; s += body) {
+#pragma unroll
+        for (int t = 0; t < body; ++t)
+          stream_step<MAXT>(q0[t % kDepth], q1[t % kDepth], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt,
+                            lane, corr_op, acc0, acc1, corr);
+      }
+      for (; s + kDepth <= S; s += kDepth) {
+#pragma unroll
+        for (int t = 0; t < kDepth; ++t)
+          stream_step<MAXT>(q0[t], q1[t], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt, lane, corr_op,
+                            acc0, acc1, corr);
+      }
+      const int rem = S - s;                                // last chunk only; issues no loads
+#pragma unroll
+      for (int d = 0; d < kDepth - 1; ++d)
+        if (d < rem) mma_step<MAXT>(q0[d], q1[d], lds, s + d, S, nt, lane, corr_op, acc0, acc1, corr);
+    }
+    sg += S;
   }
   if (!has_work) return;
 
@@ -184,10 +269,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
     const int r = seg0 + col;
     if (GATEUP) {
       const int nb = cb * 16 + 4 * g;
-      const float4 sg = *reinterpret_cast<const float4*>(ws + nb);
-      const float4 su = *reinterpret_cast<const float4*>(ws + p.n_out + nb);
+      const float4 sg4 = *reinterpret_cast<const float4*>(ws + nb);
+      const float4 su4 = *reinterpret_cast<const float4*>(ws + p.n_out + nb);
       float gv[4], uv[4], av[4];
-      const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+      const float sgv[4] = {sg4.x, sg4.y, sg4.z, sg4.w}, suv[4] = {su4.x, su4.y, su4.z, su4.w};
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         gv[v] = (acc0[j][v] + corr[j][v]) * k0 * sgv[v];
@@ -231,8 +316,8 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     p.kslice = p.K;                  // the fused epilogue needs the whole reduction
     p.ksplit = 1;
   } else {
-    // two LDS chunks per slice when an expert holds up to 16 rows
-    p.kslice = std::min(p.K, 2 * ((kDecodeLds / 32) / 128) * 128);
+    // one LDS chunk (fp16) per slice when an expert holds up to 16 rows
+    p.kslice = std::min(p.K, kDecodeLds / 32);
     p.ksplit = (p.K + p.kslice - 1) / p.kslice;
   }
 }
