@@ -95,13 +95,18 @@ def _int4_matmul(a_codes_f64, words, row_chunk=4096):
 
 
 def moe_forward(x_bits, logits, s_x, w13, w2, act, s_a, out_f32=False, tokens=None,
-                E=None):
+                E=None, a_codes_given=None):
     """Run the quantized layer (steps 1-8 of the module docstring).
 
     x_bits: bf16 bits [T, H]; logits: float32 [T, E]; s_x, s_a: fp32 static scales;
     w13: (words [E, 2I, H/8], scales [E, 2I]) or callable e -> that pair for one expert;
     w2: (words [E, H, I/8], scales [E, H]) or callable; tokens: optional subset of
-    token ids whose outputs are computed (routing and sort always cover all tokens).
+    token ids whose outputs are computed (routing and sort always cover all tokens);
+    a_codes_given: optional uint8 [2T, I] E4M3 codes indexed by sorted row. When given,
+    the down projection (step 7) reads these codes instead of requantizing this
+    oracle's own gate|up: the requantization is a rounding decision, and a caller that
+    took it from another evaluation of gate|up passes the codes it took (steps 1-6 are
+    still computed and returned as usual).
 
     Returns a dict: ids, weights, counts, offsets, sorted_pair, pair_pos (all tokens);
     rows (sorted row ids computed), h [rows, 2I] fp64, a [rows, I] fp64,
@@ -144,7 +149,8 @@ def moe_forward(x_bits, logits, s_x, w13, w2, act, s_a, out_f32=False, tokens=No
         he = acc * np.float64(s_x) * np.asarray(sc13, dtype=np.float64)[None, :]
         ae = activation(he[:, :I], act) * he[:, I:]
         ce = quantize_static(ae.astype(np.float32), s_a)
-        acc2 = _int4_matmul(e4m3_decode(ce), words2)                        # exact
+        cd = ce if a_codes_given is None else np.asarray(a_codes_given, np.uint8)[rows[sel]]
+        acc2 = _int4_matmul(e4m3_decode(cd), words2)                        # exact
         ye = acc2 * np.float64(s_a) * np.asarray(sc2, dtype=np.float64)[None, :]
         h[sel], a[sel], a_codes[sel], y[sel] = he, ae, ce, ye
 

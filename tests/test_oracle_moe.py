@@ -147,3 +147,31 @@ def test_pair_rows_and_combine_plumbing():
         assert r["sorted_pair"][r["rows"][r0]] == 2 * t
         expect = r["weights"][t, 0] * r["y"][r0] + r["weights"][t, 1] * r["y"][r1]
         assert np.array_equal(r["out"][t], expect)
+
+
+def test_given_codes_feed_the_down_projection():
+    """Codes passed in replace the requantized ones row by row: the oracle's own codes
+    give the same result, and changing one code of sorted row r, channel i moves y[r]
+    by exactly (new - old) * s_a * s_w2[e, n] * q2[e, n, i] and leaves other rows alone."""
+    cfg = synth.custom_moe("given", T=12, H=128, I=256, E=4, w_cfg=71, x_cfg=71)
+    x, logits, w13, w2 = _layer_inputs(cfg)
+    p13, p2 = w4_pack(w13), w4_pack(w2)
+    s_x, s_a = np.float32(0.01), np.float32(0.002)
+    base = moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, True)
+    assert np.array_equal(base["rows"], np.arange(2 * cfg.T))
+    same = moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, True, a_codes_given=base["a_codes"])
+    assert np.array_equal(same["y"], base["y"]) and np.array_equal(same["out"], base["out"])
+    codes = base["a_codes"].copy()
+    r, i = 7, 100
+    e = int(np.searchsorted(base["offsets"], r, side="right") - 1)
+    old = codes[r, i]
+    new = np.uint8(0x38 if old != 0x38 else 0x40)      # 1.0 or 2.0
+    codes[r, i] = new
+    got = moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, True, a_codes_given=codes)
+    q2 = w4_unpack_codes(p2[0][e], cfg.I).astype(np.float64)      # [H, I]
+    delta = (e4m3_decode(np.array([new]))[0] - e4m3_decode(np.array([old]))[0]) * np.float64(s_a)
+    expect = base["y"][r] + delta * np.asarray(p2[1][e], np.float64) * q2[:, i]
+    assert np.allclose(got["y"][r], expect, rtol=1e-13, atol=1e-12)
+    others = np.arange(2 * cfg.T) != r
+    assert np.array_equal(got["y"][others], base["y"][others])
+    assert np.array_equal(got["h"], base["h"])
