@@ -166,6 +166,65 @@ def test_moe_layer_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
+# Token counts above 64 take the tiled kernel: 256-row tiles over each expert's segment
+# (ragged last tiles, empty experts), 128-channel gate|up tiles, 256-channel down tiles.
+PREFILL_CASES = [
+    synth.custom_moe("pf_small", T=96, H=256, I=512, E=4, w_cfg=301, x_cfg=301),
+    synth.custom_moe("pf_ragged", T=300, H=640, I=384, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=302,
+                     x_cfg=302, logit_sigma=1.5),
+    synth.custom_moe("pf_multi_tile", T=700, H=1152, I=1280, E=2, w_cfg=303, x_cfg=303),
+    synth.custom_moe("pf_skewed", T=520, H=512, I=256, E=8, act=synth.ACT_GELU_TANH, w_cfg=304, x_cfg=304,
+                     expert_bias=True, logit_sigma=2.0),
+    synth.custom_moe("pf_many_experts", T=200, H=384, I=256, E=32, w_cfg=305, x_cfg=305, out_f32=False),
+    # 9 of 16 experts empty, several with a single row
+    synth.custom_moe("pf_empty_experts", T=130, H=256, I=256, E=16, w_cfg=306, x_cfg=306, expert_bias=True,
+                     logit_sigma=0.5),
+]
+
+
+@pytest.mark.parametrize("cfg", PREFILL_CASES, ids=[c.name for c in PREFILL_CASES])
+def test_moe_prefill_parity(cfg):
+    """The tiled path. gate|up to the 1e-4 bar; the requantized codes are decided on the
+    kernel's own gate|up (checked against the oracle's epilogue), and the final output is
+    held to the full bar against the oracle's down projection and combine of those codes,
+    and to the 1e-2 bar against the oracle's end-to-end result."""
+    x = synth.activations(cfg)
+    logits = synth.router_logits(cfg)
+    w13 = synth.moe_weights(cfg, "w13")
+    w2 = synth.moe_weights(cfg, "w2")
+    p13, p2 = oracle.w4_pack(w13), oracle.w4_pack(w2)
+    s_x, s_a = _oracle_scales(cfg, x, logits, p13, p2)
+    ref = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32)
+    gw13, gs13 = W.w4_pack(bf16_dev(w13))
+    gw2, gs2 = W.w4_pack(bf16_dev(w2))
+    r = W.moe_route_sort(f32_dev(logits))
+    assert np.array_equal(host(r["offsets"]), ref["offsets"])
+    print(f"{cfg.name}: rows per expert {np.diff(ref['offsets']).tolist()}", flush=True)
+    xd = bf16_dev(x)
+    a, h = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a, debug=True)
+    assert_gateup_close(host(h), ref["h"])
+    assert_codes_consistent(host(a), ref["a_codes"], host(h), cfg.act, s_a, cfg.I)
+    a2 = W.moe_gemm1_w4a8(W.fp8_quant_static(xd, s_x), s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act,
+                          s_a)
+    assert torch().equal(a, a2)
+    od = "f32" if cfg.out_f32 else "bf16"
+    out = W.moe_gemm2_w4a8(a, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"], od)
+    same = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32, a_codes_given=host(a))
+    if cfg.out_f32:
+        got, want, e2e = host(out), same["out"].astype(np.float32), ref["out"].astype(np.float32)
+    else:
+        got = bf16_bits_to_f64(host(out))
+        want, e2e = bf16_bits_to_f64(same["out_rounded"]), bf16_bits_to_f64(ref["out_rounded"])
+    assert_final_close(got, want)
+    m = np.max(np.abs(e2e))
+    d = np.abs(np.asarray(got, np.float64) - e2e)
+    print(f"end to end: max err {d.max() / m:.3g} x max|ref|, {np.mean(d > 1e-3 * m):.4%} above 1e-3", flush=True)
+    assert d.max() <= 1e-2 * m
+    a3 = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a)
+    out3 = W.moe_gemm2_w4a8(a3, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"], od)
+    assert torch().equal(a, a3) and torch().equal(out, out3)
+
+
 def test_integer_case_gate_up_bit_exact():
     """Integer x and w, max |w| = 7 per row, s_x = 1: fp32 accumulation is exact in any
     order, so gate|up must equal the integer product exactly."""
