@@ -52,11 +52,14 @@ def bf16_dev(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
+COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_prefill": "moe_prefill_grok_T32768.json"}
+
+
 def counter_traffic(workload):
     """HBM bytes per gate|up launch from the committed rocprofv3 counters, or None when
     they were taken on another workload or on a different kernel source."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"moe_decode_{workload.replace('_decode', '')}_T32.json")
+    path = os.path.join(ROOT, "profiles", COUNTER_FILES.get(workload, "-"))
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
@@ -78,10 +81,16 @@ def moe_bytes(cfg, counts):
     return layer, gemm1, touched
 
 
-def cpu_baseline(cfg, s_x, s_a, ids):
-    """The oracle on a bounded sample of the same workload: the tokens routed to the most
-    common expert pair of the batch (their two experts' weights packed by the oracle,
-    untimed); the timed part is the oracle's layer forward of those tokens."""
+def gemm1_flops(cfg):
+    """Multiply-add work of the gate|up call: every one of the 2T sorted rows against the
+    2I weight rows of its expert, K = H."""
+    return 2.0 * (2 * cfg.T) * (2 * cfg.I) * cfg.H
+
+
+def cpu_baseline(cfg, s_x, s_a, ids, max_tokens=32):
+    """The oracle on a bounded sample of the same workload: up to max_tokens of the tokens
+    routed to the most common expert pair of the batch (their two experts' weights packed
+    by the oracle, untimed); the timed part is the oracle's layer forward of those tokens."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -92,7 +101,7 @@ def cpu_baseline(cfg, s_x, s_a, ids):
     logits = synth.router_logits(cfg)
     pairs = [tuple(sorted(map(int, r))) for r in ids]
     best = max(set(pairs), key=pairs.count)
-    toks = np.array([t for t, p in enumerate(pairs) if p == best], dtype=np.int64)
+    toks = np.array([t for t, p in enumerate(pairs) if p == best], dtype=np.int64)[:max_tokens]
     packed13 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w13", e)) for e in best}
     packed2 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w2", e)) for e in best}
     t0 = time.perf_counter()
@@ -101,7 +110,7 @@ def cpu_baseline(cfg, s_x, s_a, ids):
     dt = time.perf_counter() - t0
     return {"value": float(len(toks) / dt), "unit": "tokens/s",
             "cores": int(max(1, blas_threads)), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{len(toks)} of {cfg.T} tokens (those routed to experts {best[0]} and {best[1]}), "
+            "sample": f"{len(toks)} of {cfg.T} tokens (routed to experts {best[0]} and {best[1]}), "
                       f"full oracle forward (fp64, int4 unpack, exact sums); {dt:.2f} s"}
 
 
@@ -240,7 +249,23 @@ def main():
                 "gemm1": per_launch_us(gemm1), "gemm2_combine": per_launch_us(gemm2)}
     layer_bytes, gemm1_bytes, touched = moe_bytes(cfg, counts)
     layer_us = ms_per_step * 1e3
-    g1_gbs = gemm1_bytes / per_call["gemm1"] / 1e3
+    tiled = W.moe_kernel(T) == W.KERNEL_TILED
+    if tiled:
+        # many tokens per expert: the tiled kernel is bound by the fp8 matrix cores
+        tf = gemm1_flops(cfg) / (per_call["gemm1"] * 1e-6) / 1e12
+        roofline = {"kernel": "moe_gemm1_w4a8 (moe_prefill_kernel<gate|up>)", "bound": "mfma",
+                    "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": counter_traffic(cfg.name),
+                    "flops_per_launch": gemm1_flops(cfg), "bytes_per_launch": int(gemm1_bytes)}
+        layer_flops = 2 * gemm1_flops(cfg) * 0.75         # gate|up + down (half the width of gate|up)
+        layer_frac = {"layer_mfma_frac": round(layer_flops / (layer_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+    else:
+        g1_gbs = gemm1_bytes / per_call["gemm1"] / 1e3
+        roofline = {"kernel": "moe_gemm1_w4a8 (moe_decode_kernel<gate|up>)", "bound": "hbm",
+                    "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(cfg.name),
+                    "bytes_per_launch": int(gemm1_bytes)}
+        layer_frac = {"layer_hbm_frac": round(layer_bytes / (layer_us * 1e3) / HBM_PEAK_GBS, 4)}
     result = {
         "metric": METRIC,
         "value": round(T / (ms_per_step / 1e3), 1),
@@ -257,13 +282,10 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": 2,
                    "activation": ACT_NAMES[cfg.act], "out": "fp32" if cfg.out_f32 else "bf16",
                    "weight_copies_rotated": copies, "experts_touched": touched},
-        "layer_hbm_frac": round(layer_bytes / (layer_us * 1e3) / HBM_PEAK_GBS, 4),
+        **layer_frac,
         "layer_bytes": int(layer_bytes),
         "calls_us": {k: round(v, 2) for k, v in per_call.items()},
-        "roofline": {"kernel": "moe_gemm1_w4a8 (moe_decode_kernel<gate|up>)", "bound": "hbm",
-                     "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": counter_traffic(cfg.name),
-                     "bytes_per_launch": int(gemm1_bytes)},
+        "roofline": roofline,
         "w4_pack": {"ms": round(pack_ms, 3), "GB/s": round(pack_bytes / pack_ms / 1e6, 1)},
     }
     if args.copy_ref:

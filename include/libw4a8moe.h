@@ -124,7 +124,7 @@ int32_t fp8_quant_static(const uint16_t* x_bf16, int64_t n, float s, uint8_t* ou
  *   offsets     [E+1]  int32 (out) exclusive prefix sum of counts, offsets[E] = 2T
  *   sorted_pair [2T]   int32 (out) pair ids expert by expert, increasing within an expert
  *   pair_pos    [2T]   int32 (out) inverse: sorted_pair[pair_pos[p]] == p
- * Requires 2 <= E <= 256, 0 <= T <= 2^29. T == 0 writes offsets (all 0) and counts.
+ * Requires 2 <= E <= 256, 0 <= T <= 2^22. T == 0 writes offsets (all 0) and counts.
  */
 int32_t moe_route_sort(const float* logits, int32_t T, int32_t E,
                        int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
@@ -149,7 +149,12 @@ int32_t moe_route_sort(const float* logits, int32_t T, int32_t E,
  *              h = s_x * s_w13[e][n] * sum_k x_hat[t][k] * q13[e][n][k]   (t = sorted_pair[r]/2)
  *              a_fp8[r][n] = e4m3(fp32(act(h[n]) * h[I+n]) / s_a)
  *   gateup_dbg [2T][2I] fp32 (out, optional, NULL to skip): h per sorted row
- * Requires H % 128 == 0, I % 128 == 0, 2 <= E <= 256, 0 <= T, T*H and 2T*I < 2^31.
+ * Accuracy: up to 64 tokens (w4a8_moe_kernel) the sums are exact products added in
+ * fp32; above it the fp8 matrix instruction adds each 128-long block of products with
+ * about 14 bits below its largest product, so h carries a relative error of about
+ * 1e-5 of its row's largest value, and a code of a_fp8 can then sit one step from the
+ * one an exact h gives.
+ * Requires H % 128 == 0, I % 128 == 0, 2 <= E <= 256, 0 <= T <= 2^22, 2T*H < 2^31, I*H < 2^31.
  * Workspace: w4a8_workspace_bytes(x_dtype == BF16 ? W4A8_OP_GEMM1_BF16 : W4A8_OP_GEMM1, T, H, I, E).
  */
 int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x,
@@ -171,7 +176,7 @@ int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x,
  *             Y[r][n]  = s_a * s_w2[e][n] * sum_j a_hat[r][j] * q2[e][n][j]
  *             out[t][n] = topk_w[t][0] * Y[pair_pos[2t]][n] + topk_w[t][1] * Y[pair_pos[2t+1]][n]
  *           (fp32, slot 0 first; split-K partial sums are added in a fixed order)
- * Requires H % 128 == 0, I % 128 == 0, 2 <= E <= 256, 0 <= T.
+ * Requires H % 128 == 0, I % 128 == 0, 2 <= E <= 256, 0 <= T <= 2^22, 2T*H < 2^31, I*H < 2^31.
  * Workspace: w4a8_workspace_bytes(W4A8_OP_GEMM2, T, H, I, E).
  */
 int32_t moe_gemm2_w4a8(const uint8_t* a_fp8, float s_a,
@@ -208,6 +213,14 @@ size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t 
 
 /* A static, human-readable description of a status code. */
 const char* w4a8_status_str(int32_t status);
+
+/* Which kernel the MoE GEMM calls use for T tokens (T >= 0): W4A8_KERNEL_STREAM, the
+ * weight-streaming kernel for few tokens per expert (bound by HBM), or
+ * W4A8_KERNEL_TILED, the 256 x 256 tiled kernel for many tokens per expert (bound by
+ * the fp8 matrix cores). Results of either meet the same accuracy contract. */
+#define W4A8_KERNEL_STREAM 0
+#define W4A8_KERNEL_TILED  1
+int32_t w4a8_moe_kernel(int32_t T);
 
 #ifdef __cplusplus
 }

@@ -18,9 +18,16 @@ def L():
 def test_exports_every_declared_function(L):
     names = W.header_functions()
     assert set(names) == {"w4_pack", "fp8_quant_static", "moe_route_sort", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
-                          "fp8_block_quant", "fp8_block_linear", "w4a8_workspace_bytes", "w4a8_status_str"}
+                          "fp8_block_quant", "fp8_block_linear", "w4a8_workspace_bytes", "w4a8_status_str",
+                          "w4a8_moe_kernel"}
     for n in names:
         assert hasattr(L, n), n
+
+
+def test_kernel_choice(L):
+    # up to 64 tokens the streaming kernel, above it the tiled one
+    assert [W.moe_kernel(t) for t in (0, 1, 32, 64)] == [W.KERNEL_STREAM] * 4
+    assert [W.moe_kernel(t) for t in (65, 1024, 32768)] == [W.KERNEL_TILED] * 3
 
 
 def test_status_strings(L):

@@ -42,6 +42,7 @@ _SIGNATURES = {
     "fp8_block_linear": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "w4a8_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "w4a8_status_str": (ctypes.c_char_p, [_I32]),
+    "w4a8_moe_kernel": (_I32, [_I32]),
 }
 
 
@@ -81,6 +82,14 @@ def status_str(status: int) -> str:
 
 def workspace_bytes(op, a, b, c, E) -> int:
     return int(lib().w4a8_workspace_bytes(op, a, b, c, E))
+
+
+KERNEL_STREAM, KERNEL_TILED = 0, 1
+
+
+def moe_kernel(T) -> int:
+    """KERNEL_STREAM or KERNEL_TILED: the kernel the MoE GEMM calls use for T tokens."""
+    return int(lib().w4a8_moe_kernel(T))
 
 
 # ------------------------------------------------------------------ torch wrappers

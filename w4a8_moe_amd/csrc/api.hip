@@ -29,9 +29,7 @@ int32_t check_moe_shape(int32_t T, int32_t H, int32_t I, int32_t E) {
   if (T < 0 || T > kMaxRouteTokens) return W4A8_ERR_SHAPE;
   if (E < 2 || E > W4A8_MAX_EXPERTS) return W4A8_ERR_SHAPE;
   if (H <= 0 || I <= 0 || H % 128 != 0 || I % 128 != 0) return W4A8_ERR_SHAPE;
-  if ((int64_t)T * H >= (int64_t(1) << 31) || (int64_t)2 * T * I >= (int64_t(1) << 31) ||
-      (int64_t)2 * T * H >= (int64_t(1) << 31))
-    return W4A8_ERR_SHAPE;
+  if ((int64_t)2 * T * H >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;   // x, partials: 32-bit offsets
   if ((int64_t)E * 2 * I * (H / 8) >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
   if ((int64_t)I * H >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;   // one expert's packed matrix < 2 GiB
   return W4A8_OK;
@@ -69,6 +67,8 @@ const char* w4a8_status_str(int32_t status) {
     default: return "unknown status";
   }
 }
+
+int32_t w4a8_moe_kernel(int32_t T) { return decode_fits(T) ? W4A8_KERNEL_STREAM : W4A8_KERNEL_TILED; }
 
 size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t I_or_K, int32_t E) {
   switch (op) {

@@ -8,47 +8,72 @@
 // MFMA (16x16x128), accumulating in fp32; the per-channel and static scales are applied
 // in the epilogue.
 //
-// Tile. A workgroup computes 256 sorted rows (tokens of one expert) x 256 weight rows,
-// K in steps of 128, with 4 waves of 128 x 128 each. For gate|up the 256 weight rows are
-// 128 gate channels and the 128 matching up channels, and each wave holds 64 of each, so
-// act(gate) * up is formed in registers. Per k-step the workgroup
-//  * loads the token tile (256 x 128 E4M3 codes, gathered through sorted_pair for
-//    gate|up) and the weight tile (256 x 64 bytes of int4),
-//  * converts every weight code once to E4M3 (v_perm table lookup, exact for all 16
-//    two's-complement codes) and stores both tiles in LDS in MFMA operand order
-//    (lane l reads 16 contiguous bytes, 1 KB per wave instruction),
-//  * and runs 64 MFMAs per wave.
-// The next k-step's global loads are issued before the MFMAs of the current one.
+// Tile. A workgroup computes 192 sorted rows (tokens of one expert) x 256 weight rows,
+// K in steps of 128, with 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against
+// all 192 tokens (12 blocks), so its int4 codes go from global memory straight into its
+// own registers, are converted there (v_perm table lookup, exact for all 16
+// two's-complement codes) and are used as MFMA operands without an LDS round trip. For
+// gate|up the 64 rows are 32 gate channels and the 32 matching up channels, so
+// act(gate) * up is formed in registers. Only the token tile (192 x 128 E4M3 codes per
+// k-step, gathered through sorted_pair for gate|up) is shared through LDS, double
+// buffered, in MFMA operand order with an XOR swizzle that keeps both the staging writes
+// and the operand reads free of bank conflicts.
+//
+// Pipeline, per k-step s (one barrier each):
+//   * store the tokens of step s+1 (loaded one step earlier) into the other LDS buffer,
+//     issue the token loads of step s+2,
+//   * 64 MFMAs of step s, with the conversion of step s+1's weights (loaded two steps
+//     earlier) and the weight loads of step s+3 in between.
+// Loads past the last k-step read in-bounds data or zeros and are never used, so the
+// loop has no branches.
+//
 // Accumulation note: gfx950's fp8 MFMA keeps about 14 bits below the largest product of
 // an instruction, so results differ from exact fp32 sums by about 1e-5 of the row scale.
 #include <algorithm>
+#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
 
 namespace w4a8 {
 
-constexpr int kPM = 256;          // sorted rows per tile
+constexpr int kTB = 12;           // token blocks of 16 rows per tile
+constexpr int kPM = 16 * kTB;     // sorted rows per tile
 constexpr int kPN = 256;          // weight rows per tile
-constexpr int kPThreads = 256;    // 4 waves, 2 x 2 of 128 x 128
-constexpr int kPTileBytes = 16 * 2048;                    // 16 blocks of 16 rows x 128 codes
-constexpr int kPLds = 2 * kPTileBytes;                     // tokens, then weights
-constexpr int kGroupM = 8;        // M-tiles per band of the tile order
+constexpr int kPThreads = 256;    // 4 waves, 64 weight rows each
+constexpr int kTJ = kPM * 8 / kPThreads;                  // 16-byte token chunks per thread and k-step
+constexpr int kPTokBytes = kTB * 2048;                    // blocks of 16 rows x 128 codes
+constexpr int kPLds = 2 * kPTokBytes;                      // two token buffers
+constexpr int kGroupM = 4;        // M-tiles per band of the tile order
+constexpr int kWRing = 3;         // k-steps of raw weights in flight per wave
 constexpr uint32_t kPOutOfRange = 0x80000000u;   // past every buffer (all are < 2^31 bytes)
 
 __device__ __forceinline__ uint4 pf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Four two's-complement nibbles (bits 0..3 of each byte, other bits zero) -> four exact
-// E4M3 codes: 0..7 -> 00 38 40 44 48 4A 4C 4E, -8..-1 -> D0 CE CC CA C8 C4 C0 B8.
-__device__ __forceinline__ uint32_t nib4_to_e4m3(uint32_t x) {
-  const uint32_t sel = x & 0x07070707u;
+// Four two's-complement nibbles -> four exact E4M3 codes: 0..7 -> 00 38 40 44 48 4A 4C 4E,
+// -8..-1 -> D0 CE CC CA C8 C4 C0 B8. Per byte, sel = nibble & 7 and sgn = nibble >> 3.
+__device__ __forceinline__ uint32_t e4m3_of_nibbles(uint32_t sel, uint32_t sgn) {
   const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
   const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
   // selector 12 reads as 0x00, 13 as 0xFF: a byte mask of the sign bits
-  const uint32_t msk = __builtin_amdgcn_perm(0u, 0u, ((x >> 3) & 0x01010101u) | 0x0C0C0C0Cu);
+  const uint32_t msk = __builtin_amdgcn_perm(0u, 0u, sgn | 0x0C0C0C0Cu);
   return (msk & neg) | (~msk & pos);
+}
+
+// 16 bytes of packed int4 (32 K-values; in each word, byte b holds element b in its low
+// nibble and element 4+b in its high nibble) -> the 8 registers of an MFMA operand, in
+// natural K order.
+__device__ __forceinline__ v8i int4x32_to_e4m3(uint4 q) {
+  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+  v8i a;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    a[2 * t] = (int)e4m3_of_nibbles(w[t] & 0x07070707u, (w[t] >> 3) & 0x01010101u);
+    a[2 * t + 1] = (int)e4m3_of_nibbles((w[t] >> 4) & 0x07070707u, (w[t] >> 7) & 0x01010101u);
+  }
+  return a;
 }
 
 struct TileOrigin {
@@ -70,14 +95,19 @@ __device__ __forceinline__ bool locate_mtile(const int32_t* __restrict__ offsets
   return false;
 }
 
+// LDS position of the 16 bytes that lane (row i, K-part g) reads in half h of a token
+// block: 16-byte slot 16 g + (i ^ (2 g + 8 h)) of the half's 1 KB. Within 16 consecutive
+// reading lanes the slots are distinct mod 16 (no bank conflict); so are they for 16
+// consecutive staging lanes (two rows x four K-parts x two halves).
+__device__ __forceinline__ int tok_slot(int i, int g, int h) { return 16 * g + (i ^ (2 * g + 8 * h)); }
+
 template <bool GATEUP>
 __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  uint8_t* ldsT = lds;
-  uint8_t* ldsW = lds + kPTileBytes;
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
-  const int wm = wave & 1, wn = wave >> 1;
+  const int i = lane & 15, g = lane >> 4;
+
   // Tile order. Workgroups are dispatched round-robin over the 8 XCDs, so workgroup b runs
   // on XCD b % 8; each XCD gets a contiguous run of the tile order, and the order walks
   // bands of kGroupM M-tiles, all N-tiles of a band before the next band. The workgroups
@@ -91,118 +121,146 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   TileOrigin o;
   if (!locate_mtile(p.offsets, p.E, mt, o)) return;
   const int rows = min(kPM, o.cnt - o.m0);                  // valid sorted rows in this tile
-  // weight rows of the tile: gate|up -> 128 gate channels + the 128 matching up channels
+  // first channel of the tile: gate|up -> 128 channels (gate rows + the matching up rows)
   const int n0 = GATEUP ? ntile * (kPN / 2) : ntile * kPN;
 
-  // ---- per-thread load assignment (fixed for the whole K loop). Raw buffer loads: rows
-  // outside the tile get an offset past the buffer's end and read as zeros.
-  // weights: 1024 chunks of 16 bytes per k-step, chunk c = tid + 256 j: tile row c/4, part c%4
+  // ---- this lane's weight rows: block a of the wave, row i of the block, K-part g
   const uint32_t row_bytes = (uint32_t)p.K / 2;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const uint8_t*>(p.w) + (size_t)o.e * p.Nw * row_bytes), (short)0,
       (int)(p.Nw * row_bytes), 0x00020000);
   uint32_t woff[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = tid + kPThreads * j, rho = c >> 2, part = c & 3;
-    const int half = GATEUP && rho >= kPN / 2;
-    const int chan = n0 + rho - half * (kPN / 2);
-    const int grow = chan + half * p.n_out;
-    woff[j] = chan < (GATEUP ? p.n_out : p.Nw) ? (uint32_t)grow * row_bytes + part * 16 : kPOutOfRange;
+  for (int a = 0; a < 4; ++a) {
+    // gate|up: blocks 0,1 gate channels n0 + 32 w + 16 (a % 2) + i, blocks 2,3 their up rows
+    const int chan = GATEUP ? n0 + 32 * wave + 16 * (a & 1) + i : n0 + 64 * wave + 16 * a + i;
+    const int grow = GATEUP && a >= 2 ? chan + p.n_out : chan;
+    woff[a] = chan < (GATEUP ? p.n_out : p.Nw) ? (uint32_t)grow * row_bytes + 16 * g : kPOutOfRange;
   }
-  // tokens: 2048 chunks of 16 bytes per k-step, chunk c = tid + 256 j: tile row c/8, part c%8
+
+  // ---- token staging: chunk c = tid + 256 j is tile row c / 8, 16-byte part c % 8.
+  // gate|up gathers token rows of x (T*H < 2^31 bytes); down reads the tile's own rows of
+  // the sorted activation (the buffer starts at the tile, kPM*K < 2^31 bytes).
+  const uint8_t* tbase = GATEUP ? p.act : p.act + (size_t)(o.seg0 + o.m0) * p.K;
   const __amdgpu_buffer_rsrc_t tr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)p.act, (short)0, (int)((GATEUP ? p.P / 2 : p.P) * p.K), 0x00020000);
-  uint32_t toff[8];
+      (void*)tbase, (short)0, (int)((GATEUP ? p.P / 2 : rows) * p.K), 0x00020000);
+  uint32_t toff[kTJ];
+  int tdst[kTJ];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < kTJ; ++j) {
     const int c = tid + kPThreads * j, r = c >> 3, part = c & 7;
     uint32_t off = kPOutOfRange;
     if (r < rows) {
-      const int srow = GATEUP ? (p.sorted_pair[o.seg0 + o.m0 + r] >> 1) : (o.seg0 + o.m0 + r);
+      const int srow = GATEUP ? (p.sorted_pair[o.seg0 + o.m0 + r] >> 1) : r;
       off = (uint32_t)srow * p.K + part * 16;
     }
     toff[j] = off;
+    const int pg = part >> 1, ph = part & 1;
+    tdst[j] = (r >> 4) * 2048 + ph * 1024 + tok_slot(r & 15, pg, ph) * 16;
   }
+  const int rd0 = tok_slot(i, g, 0) * 16, rd1 = 1024 + tok_slot(i, g, 1) * 16;
 
-  v4f acc[8][8];
+  v4f acc[kTB][4];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int bb = 0; bb < kTB; ++bb)
 #pragma unroll
-    for (int b = 0; b < 8; ++b) acc[a][b] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  uint4 wq[4], tq[8];
-  // an out-of-range offset stays out of range after adding k (offsets < 2^31, k < 2^30)
-  auto load_step = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) wq[j] = pf_ld16(wr, woff[j] + (uint32_t)(k0 / 2));
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tq[j] = pf_ld16(tr, toff[j] + (uint32_t)k0);
-  };
+    for (int a = 0; a < 4; ++a) acc[bb][a] = v4f{0.f, 0.f, 0.f, 0.f};
 
   const int steps = p.K / 128;
-  load_step(0);
-  for (int s = 0; s < steps; ++s) {
-    // convert this step's weights (exact E4M3 codes)
-    uint4 wc[4][2];
+  // an out-of-range offset stays out of range after adding k (offsets < 2^31, k < 2^30)
+  uint4 tq[kTJ];
+  auto load_tokens = [&](int s) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t w[4] = {wq[j].x, wq[j].y, wq[j].z, wq[j].w};
-      uint32_t cd[8];
+    for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16(tr, toff[j] + (uint32_t)(s * 128));
+  };
+  auto store_tokens = [&](int buf) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        cd[2 * t] = nib4_to_e4m3(w[t] & 0x0F0F0F0Fu);
-        cd[2 * t + 1] = nib4_to_e4m3((w[t] >> 4) & 0x0F0F0F0Fu);
+    for (int j = 0; j < kTJ; ++j) *reinterpret_cast<uint4*>(lds + buf * kPTokBytes + tdst[j]) = tq[j];
+  };
+  uint4 wq[kWRing][4];
+  auto load_weights = [&](int slot, int s) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) wq[slot][a] = pf_ld16(wr, woff[a] + (uint32_t)(s * 64));
+  };
+
+  // ---- prologue: weights of steps 0..2 in flight, tokens of step 0 in LDS, of step 1 in flight
+#pragma unroll
+  for (int s = 0; s < kWRing; ++s) load_weights(s, s);
+  load_tokens(0);
+  store_tokens(0);
+  load_tokens(1);
+  v8i aop[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) aop[a] = int4x32_to_e4m3(wq[0][a]);
+  __syncthreads();
+
+  // One k-step; SLOT = s % kWRing is a constant so that the weight ring stays in
+  // registers. The token blocks are walked with the next block's operand read ahead;
+  // into each block's 4 MFMAs go one token store (step s+1) or one token load (step s+2),
+  // one or two of the 16 words of the step s+1 weight conversion, and in the first 4 a
+  // weight load of step s+3; scheduling barriers keep the compiler from hoisting every
+  // LDS read to the top.
+  auto kstep = [&](int s, auto slot_tag) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    constexpr int NSLOT = (SLOT + 1) % kWRing;
+    const int cur = s & 1;
+    const uint8_t* T = lds + cur * kPTokBytes;
+    uint8_t* Tn = lds + (cur ^ 1) * kPTokBytes;
+    v8i anext[4];
+    v8i bcur = operand_from(*reinterpret_cast<const uint4*>(T + rd0), *reinterpret_cast<const uint4*>(T + rd1));
+#pragma unroll
+    for (int bb = 0; bb < kTB; ++bb) {
+      v8i bnext;
+      if (bb < kTB - 1)
+        bnext = operand_from(*reinterpret_cast<const uint4*>(T + (bb + 1) * 2048 + rd0),
+                             *reinterpret_cast<const uint4*>(T + (bb + 1) * 2048 + rd1));
+#pragma unroll
+      for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_fp8_16x16x128(aop[a], bcur, acc[bb][a]);
+      const int j = bb >> 1;
+      if ((bb & 1) == 0)
+        *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                     // step s+1
+      else
+        tq[j] = pf_ld16(tr, toff[j] + (uint32_t)((s + 2) * 128));             // step s+2
+      if (bb < 4) wq[SLOT][bb] = pf_ld16(wr, woff[bb] + (uint32_t)((s + kWRing) * 64));
+#pragma unroll
+      for (int wi = bb; wi < 16; wi += kTB) {
+        const int a = wi >> 2, tw = wi & 3;
+        const uint32_t w = tw == 0 ? wq[NSLOT][a].x : tw == 1 ? wq[NSLOT][a].y : tw == 2 ? wq[NSLOT][a].z
+                                                                                         : wq[NSLOT][a].w;
+        anext[a][2 * tw] = (int)e4m3_of_nibbles(w & 0x07070707u, (w >> 3) & 0x01010101u);
+        anext[a][2 * tw + 1] = (int)e4m3_of_nibbles((w >> 4) & 0x07070707u, (w >> 7) & 0x01010101u);
       }
-      wc[j][0] = make_uint4(cd[0], cd[1], cd[2], cd[3]);
-      wc[j][1] = make_uint4(cd[4], cd[5], cd[6], cd[7]);
-    }
-    __syncthreads();                                        // previous step's reads are done
-    // store both tiles in MFMA operand order: block b (16 rows) = [h][lane][16 B]
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int c = tid + kPThreads * j, rho = c >> 2, part = c & 3;
-      uint8_t* d = ldsW + (rho >> 4) * 2048 + ((rho & 15) + 16 * part) * 16;
-      *reinterpret_cast<uint4*>(d) = wc[j][0];
-      *reinterpret_cast<uint4*>(d + 1024) = wc[j][1];
+      __builtin_amdgcn_sched_barrier(0);
+      if (bb < kTB - 1) bcur = bnext;
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int c = tid + kPThreads * j, r = c >> 3, part = c & 7;
-      const int g = part >> 1, h = part & 1;
-      *reinterpret_cast<uint4*>(ldsT + (r >> 4) * 2048 + h * 1024 + ((r & 15) + 16 * g) * 16) = tq[j];
-    }
+    for (int a = 0; a < 4; ++a) aop[a] = anext[a];
     __syncthreads();
-    if (s + 1 < steps) load_step((s + 1) * 128);            // in flight during the MFMAs
-    // ---- MFMAs: token blocks 8wm.., weight blocks of this wave
-    v8i bt[8];
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-      const uint8_t* q = ldsT + (8 * wm + b) * 2048 + lane * 16;
-      bt[b] = operand_from(*reinterpret_cast<const uint4*>(q), *reinterpret_cast<const uint4*>(q + 1024));
-    }
-#pragma unroll
-    for (int a = 0; a < 8; ++a) {
-      const int wb = GATEUP ? (a < 4 ? 4 * wn + a : 8 + 4 * wn + (a - 4)) : 8 * wn + a;
-      const uint8_t* q = ldsW + wb * 2048 + lane * 16;
-      const v8i aw = operand_from(*reinterpret_cast<const uint4*>(q), *reinterpret_cast<const uint4*>(q + 1024));
-#pragma unroll
-      for (int b = 0; b < 8; ++b) acc[a][b] = mfma_fp8_16x16x128(aw, bt[b], acc[a][b]);
-    }
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  static_assert(kWRing == 3, "the loop below is unrolled by the ring size");
+  int s = 0;
+  for (; s + 3 <= steps; s += 3) {
+    kstep(s, S0{});
+    kstep(s + 1, S1{});
+    kstep(s + 2, S2{});
   }
+  if (s < steps) kstep(s, S0{});
+  if (s + 1 < steps) kstep(s + 1, S1{});
 
   // ---- epilogue: lane holds weight rows 4g..4g+3 of each block, token column i
-  const int i = lane & 15, g = lane >> 4;
   const float* ws = p.w_scale + (size_t)o.e * p.Nw;
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int rt = 128 * wm + 16 * b + i;                  // row within the tile
+  for (int bb = 0; bb < kTB; ++bb) {
+    const int rt = 16 * bb + i;                              // row within the tile
     if (rt >= rows) continue;
-    const int r = o.seg0 + o.m0 + rt;                       // sorted row
+    const int r = o.seg0 + o.m0 + rt;                        // sorted row
     if (GATEUP) {
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int nb = n0 + 64 * wn + 16 * a + 4 * g;       // channel
+      for (int a = 0; a < 2; ++a) {
+        const int nb = n0 + 32 * wave + 16 * a + 4 * g;      // channel
         if (nb >= p.n_out) continue;
         const float4 sg = *reinterpret_cast<const float4*>(ws + nb);
         const float4 su = *reinterpret_cast<const float4*>(ws + p.n_out + nb);
@@ -210,8 +268,8 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
         float gv[4], uv[4], av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          gv[v] = acc[a][b][v] * p.s_act * sgv[v];
-          uv[v] = acc[a + 4][b][v] * p.s_act * suv[v];
+          gv[v] = acc[bb][a][v] * p.s_act * sgv[v];
+          uv[v] = acc[bb][a + 2][v] * p.s_act * suv[v];
           av[v] = act_fn(gv[v], p.act_fn) * uv[v] / p.s_a;
         }
         *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
@@ -223,15 +281,15 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
       }
     } else {
 #pragma unroll
-      for (int a = 0; a < 8; ++a) {
-        const int nb = n0 + 128 * wn + 16 * a + 4 * g;
+      for (int a = 0; a < 4; ++a) {
+        const int nb = n0 + 64 * wave + 16 * a + 4 * g;
         if (nb >= p.Nw) continue;
         const float4 sw = *reinterpret_cast<const float4*>(ws + nb);
         float4 out;
-        out.x = acc[a][b][0] * p.s_act * sw.x;
-        out.y = acc[a][b][1] * p.s_act * sw.y;
-        out.z = acc[a][b][2] * p.s_act * sw.z;
-        out.w = acc[a][b][3] * p.s_act * sw.w;
+        out.x = acc[bb][a][0] * p.s_act * sw.x;
+        out.y = acc[bb][a][1] * p.s_act * sw.y;
+        out.z = acc[bb][a][2] * p.s_act * sw.z;
+        out.w = acc[bb][a][3] * p.s_act * sw.w;
         *reinterpret_cast<float4*>(p.partial + (size_t)r * p.n_out + nb) = out;
       }
     }
