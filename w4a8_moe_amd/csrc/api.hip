@@ -35,6 +35,7 @@ int32_t check_moe_shape(int32_t T, int32_t H, int32_t I, int32_t E) {
   return W4A8_OK;
 }
 
+// gemm1 workspace: the quantized x (bf16 input only)
 size_t gemm1_ws(int32_t T, int32_t H, bool bf16_x) { return bf16_x ? round_up((size_t)T * H, 256) : 0; }
 
 // gemm2's split-K partials: the same plan the launch uses.
@@ -46,6 +47,7 @@ int gemm2_ksplit(int32_t T, int32_t H, int32_t I, int32_t E) {
   return p.ksplit;
 }
 
+// gemm2 workspace: the split-K partials of the down projection
 size_t gemm2_ws(int32_t T, int32_t H, int32_t I, int32_t E) {
   return round_up((size_t)gemm2_ksplit(T, H, I, E) * 2 * T * H * sizeof(float), 256);
 }
@@ -159,7 +161,7 @@ int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x, const int32_t*
   MoeGemmParams p{};
   p.act = xq; p.w = w13; p.w_scale = s_w13; p.offsets = offsets; p.sorted_pair = sorted_pair;
   p.E = E; p.K = H; p.Nw = 2 * I; p.n_out = I; p.P = 2 * T;
-  p.s_act = s_x; p.act_fn = act; p.s_a = s_a; p.a_out = a_fp8; p.dbg = gateup_dbg;
+  p.s_act = s_x; p.act_fn = act; p.s_a = s_a; p.inv_s_a = 1.0f / s_a; p.a_out = a_fp8; p.dbg = gateup_dbg;
   if (decode) {
     plan_decode(p, true);
     launch_moe_decode(p, true, s);

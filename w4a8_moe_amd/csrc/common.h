@@ -9,6 +9,7 @@ namespace w4a8 {
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v2f __attribute__((ext_vector_type(2)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kWave = 64;
@@ -50,33 +51,6 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(v8bf a, v8bf b, v4f c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// int4 -> E4M3 in registers, "offset" form used by the streaming (decode) kernels.
-// In the reorder packing, byte b of a word holds elements b (low nibble) and 4+b (high
-// nibble). XOR with 0x8 turns a two's-complement nibble q into q + 8 in [0, 15], and the
-// E4M3 code c in [0, 15] has the value c * 2^-9 (subnormals then the first binade), so the
-// two words below are exact E4M3 codes of (q + 8) * 2^-9 for elements 0..3 and 4..7.
-// The MFMA then yields 2^-9 * sum x (q + 8); a second MFMA of the same B operand against
-// the constant code 0x88 (= -8 * 2^-9) removes the offset.
-__device__ __forceinline__ void int4x8_to_e4m3_offset(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  uint32_t y = w ^ 0x88888888u;
-  lo = y & 0x0F0F0F0Fu;
-  hi = (y >> 4) & 0x0F0F0F0Fu;
-}
-
-constexpr uint32_t kOffsetCorrCode = 0x88888888u;   // four E4M3 codes of -2^-6 = -8 * 2^-9
-
-// 16 bytes of packed int4 (32 K-values, natural K order after unpacking) -> the 8
-// registers of an MFMA operand in offset form.
-__device__ __forceinline__ v8i int4x32_to_operand_offset(uint4 q) {
-  v8i a;
-  uint32_t lo, hi;
-  int4x8_to_e4m3_offset(q.x, lo, hi); a[0] = (int)lo; a[1] = (int)hi;
-  int4x8_to_e4m3_offset(q.y, lo, hi); a[2] = (int)lo; a[3] = (int)hi;
-  int4x8_to_e4m3_offset(q.z, lo, hi); a[4] = (int)lo; a[5] = (int)hi;
-  int4x8_to_e4m3_offset(q.w, lo, hi); a[6] = (int)lo; a[7] = (int)hi;
-  return a;
-}
-
 __device__ __forceinline__ v8i operand_from(uint4 lo, uint4 hi) {
   v8i b;
   b[0] = (int)lo.x; b[1] = (int)lo.y; b[2] = (int)lo.z; b[3] = (int)lo.w;
@@ -84,11 +58,63 @@ __device__ __forceinline__ v8i operand_from(uint4 lo, uint4 hi) {
   return b;
 }
 
-__device__ __forceinline__ float act_fn(float g, int act) {
-  if (act == 0) return g / (1.0f + expf(-g));                        // silu
-  if (act == 1) return 0.5f * g * (1.0f + erff(g * 0.70710678118654752f));  // gelu (erf)
-  const float c = 0.7978845608028654f;                                // sqrt(2/pi)
-  return 0.5f * g * (1.0f + tanhf(c * (g + 0.044715f * g * g * g))); // gelu (tanh)
+// Gated activations for the epilogues, fp32 and branch-free (lanes of a wave take
+// different signs and ranges, so range-split library functions run every branch). The
+// relative error is about 1e-6 or less wherever the result is large enough to reach an
+// E4M3 code, so an exact-arithmetic activation rounds to a different code only when the
+// value sits within that distance of a rounding boundary.
+//   ACT 0, silu:      g * sigma(g),            sigma(y) = 1 / (1 + 2^(-y log2 e))
+//   ACT 1, gelu_erf:  g * Phi(g), Phi from erfc(|g|/sqrt 2) = t 2^(Q(t) - g^2 log2(e) / 2),
+//                     t = 1 / (1 + |g| / (2 sqrt 2)), Q a degree-9 polynomial fitted here
+//                     (least squares in Chebyshev form on |g| in [0, 17], max error 8e-8
+//                     in log2 units); Phi = 1 - erfc/2 for g >= 0, erfc/2 below
+//   ACT 2, gelu_tanh: g/2 (1 + tanh(y)) = g * sigma(2 y), y = sqrt(2/pi) (g + 0.044715 g^3)
+__device__ __forceinline__ float sigmoid_fast(float y) {
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * 1.4426950408889634f));
+}
+
+template <int ACT>
+__device__ __forceinline__ float act_fast(float g) {
+  if (ACT == 0) return g * sigmoid_fast(g);
+  if (ACT == 2) {
+    const float y = 0.7978845608028654f * __builtin_fmaf(0.044715f * g * g, g, g);
+    return g * sigmoid_fast(2.0f * y);
+  }
+  const float a = __builtin_fabsf(g);
+  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(a, 0.35355339059327373f, 1.0f));
+  float q = 0.22225850820541382f;
+  q = __builtin_fmaf(q, t, -1.0541905164718628f);
+  q = __builtin_fmaf(q, t, 1.8387916088104248f);
+  q = __builtin_fmaf(q, t, -1.2315798997879028f);
+  q = __builtin_fmaf(q, t, 0.07272530347108841f);
+  q = __builtin_fmaf(q, t, -0.0986909419298172f);
+  q = __builtin_fmaf(q, t, 0.08420290797948837f);
+  q = __builtin_fmaf(q, t, 0.5506213307380676f);
+  q = __builtin_fmaf(q, t, 1.4415581226348877f);
+  q = __builtin_fmaf(q, t, -1.8256964683532715f);
+  const float half_erfc = 0.5f * t * __builtin_amdgcn_exp2f(__builtin_fmaf(-g * g, 0.7213475204444817f, q));
+  return g * (g >= 0.0f ? 1.0f - half_erfc : half_erfc);
+}
+
+__device__ __forceinline__ float act_fast_rt(float g, int act) {
+  return act == 0 ? act_fast<0>(g) : act == 1 ? act_fast<1>(g) : act_fast<2>(g);
+}
+
+// x / s rounded to nearest, from r = the correctly rounded 1 / s (computed on the host):
+// q = x r is within an ulp of the quotient, the fma gives its exact residual, and one
+// correction step rounds correctly for quotients in the normal range.
+__device__ __forceinline__ float div_rn(float x, float s, float r) {
+  const float q = x * r;
+  return __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+}
+
+// Barrier for LDS hand-off only: waits for this wave's LDS operations, not for its
+// outstanding global loads (a prefetch stays in flight across it; __syncthreads would
+// wait for every load first).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }

@@ -34,7 +34,7 @@ struct MoeGemmParams {
   float s_act;                 // static scale of the activation rows
   // gate|up epilogue
   int act_fn;
-  float s_a;
+  float s_a, inv_s_a;          // inv_s_a = 1 / s_a correctly rounded (host division)
   uint8_t* a_out;              // [P][I]
   float* dbg;                  // [P][2I] or nullptr
   // down epilogue
@@ -58,7 +58,6 @@ void plan_decode(MoeGemmParams& p, bool gateup);
 void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 bool prefill_available();
-size_t prefill_gemm2_partial_bytes(int T, int H);
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 // combine: out[t] = w0 * sum_s partial[s][pair_pos[2t]] + w1 * sum_s partial[s][pair_pos[2t+1]]

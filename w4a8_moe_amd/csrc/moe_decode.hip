@@ -94,13 +94,6 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kWeightLoadAux));
 }
 
-// Barrier for LDS hand-off only: waits for this wave's LDS operations, not for its
-// outstanding global loads (the weight prefetch stays in flight across it).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
 
 // One k-step (128 K) of one wave: 4 MFMAs of K = 32 per weight block and column tile,
 // plus the offset correction, B read from the fp16 LDS chunk.
@@ -277,7 +270,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
       for (int v = 0; v < 4; ++v) {
         gv[v] = (acc0[j][v] + corr[j][v]) * k0 * sgv[v];
         uv[v] = (acc1[j][v] + corr[j][v]) * k0 * suv[v];
-        av[v] = act_fn(gv[v], p.act_fn) * uv[v] / p.s_a;
+        av[v] = div_rn(act_fast_rt(gv[v], p.act_fn) * uv[v], p.s_a, p.inv_s_a);
       }
       *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
       if (p.dbg) {

@@ -8,11 +8,20 @@
 // MFMA (16x16x128), accumulating in fp32; the per-channel and static scales are applied
 // in the epilogue.
 //
+// Conversion. Each int4 code becomes its exact E4M3 code by a table lookup on the byte
+// permute unit: for the 4 low (or high) nibbles of a word, one v_perm picks the codes of
+// 0..7, one the codes of -8..-1, and a third picks between them by the sign bit. The
+// products are then the exact q * x, so the accumulation error is that of the fp8
+// instruction on these products alone. (Offset codes q + 8, three bit operations per
+// word, would need the row sums of x taken back out, and the instruction's error grows
+// with the sum of |products|, about six times larger with the offset: that failed the
+// output tolerance.)
+//
 // Tile. A workgroup computes 192 sorted rows (tokens of one expert) x 256 weight rows,
 // K in steps of 128, with 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against
 // all 192 tokens (12 blocks), so its int4 codes go from global memory straight into its
-// own registers, are converted there (v_perm table lookup, exact for all 16
-// two's-complement codes) and are used as MFMA operands without an LDS round trip. For
+// own registers, are converted there and are used as MFMA operands without an LDS round
+// trip. For
 // gate|up the 64 rows are 32 gate channels and the 32 matching up channels, so
 // act(gate) * up is formed in registers. Only the token tile (192 x 128 E4M3 codes per
 // k-step, gathered through sorted_pair for gate|up) is shared through LDS, double
@@ -30,7 +39,6 @@
 // Accumulation note: gfx950's fp8 MFMA keeps about 14 bits below the largest product of
 // an instruction, so results differ from exact fp32 sums by about 1e-5 of the row scale.
 #include <algorithm>
-#include <type_traits>
 
 #include "common.h"
 #include "kernels.h"
@@ -45,33 +53,38 @@ constexpr int kTJ = kPM * 8 / kPThreads;                  // 16-byte token chunk
 constexpr int kPTokBytes = kTB * 2048;                    // blocks of 16 rows x 128 codes
 constexpr int kPLds = 2 * kPTokBytes;                      // two token buffers
 constexpr int kGroupM = 4;        // M-tiles per band of the tile order
-constexpr int kWRing = 3;         // k-steps of raw weights in flight per wave
 constexpr uint32_t kPOutOfRange = 0x80000000u;   // past every buffer (all are < 2^31 bytes)
 
 __device__ __forceinline__ uint4 pf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
-// Four two's-complement nibbles -> four exact E4M3 codes: 0..7 -> 00 38 40 44 48 4A 4C 4E,
-// -8..-1 -> D0 CE CC CA C8 C4 C0 B8. Per byte, sel = nibble & 7 and sgn = nibble >> 3.
+// Four two's-complement nibbles (sel = nibble & 7 per byte, sgn = 4 * sign bit per byte)
+// -> four exact E4M3 codes: 0..7 -> 00 38 40 44 48 4A 4C 4E, -8..-1 -> D0 CE CC CA C8 C4
+// C0 B8. The last permute takes byte i from the positive (selector i) or the negative
+// (selector 4 + i) table.
 __device__ __forceinline__ uint32_t e4m3_of_nibbles(uint32_t sel, uint32_t sgn) {
   const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
   const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
-  // selector 12 reads as 0x00, 13 as 0xFF: a byte mask of the sign bits
-  const uint32_t msk = __builtin_amdgcn_perm(0u, 0u, sgn | 0x0C0C0C0Cu);
-  return (msk & neg) | (~msk & pos);
+  return __builtin_amdgcn_perm(neg, pos, sgn | 0x03020100u);
 }
 
-// 16 bytes of packed int4 (32 K-values; in each word, byte b holds element b in its low
-// nibble and element 4+b in its high nibble) -> the 8 registers of an MFMA operand, in
-// natural K order.
+// One packed word (byte b: element b in the low nibble, element 4+b in the high nibble)
+// -> E4M3 codes of elements 0..3 (lo) and 4..7 (hi).
+__device__ __forceinline__ void int4x8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t& hi) {
+  lo = e4m3_of_nibbles(w & 0x07070707u, (w >> 1) & 0x04040404u);
+  hi = e4m3_of_nibbles((w >> 4) & 0x07070707u, (w >> 5) & 0x04040404u);
+}
+
 __device__ __forceinline__ v8i int4x32_to_e4m3(uint4 q) {
   const uint32_t w[4] = {q.x, q.y, q.z, q.w};
   v8i a;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    a[2 * t] = (int)e4m3_of_nibbles(w[t] & 0x07070707u, (w[t] >> 3) & 0x01010101u);
-    a[2 * t + 1] = (int)e4m3_of_nibbles((w[t] >> 4) & 0x07070707u, (w[t] >> 7) & 0x01010101u);
+    uint32_t lo, hi;
+    int4x8_to_e4m3(w[t], lo, hi);
+    a[2 * t] = (int)lo;
+    a[2 * t + 1] = (int)hi;
   }
   return a;
 }
@@ -101,7 +114,9 @@ __device__ __forceinline__ bool locate_mtile(const int32_t* __restrict__ offsets
 // consecutive staging lanes (two rows x four K-parts x two halves).
 __device__ __forceinline__ int tok_slot(int i, int g, int h) { return 16 * g + (i ^ (2 * g + 8 * h)); }
 
-template <bool GATEUP>
+// ACT: the gated activation (gate|up only), a template parameter so that each instance
+// carries the code of one activation in its unrolled epilogue.
+template <bool GATEUP, int ACT>
 __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id();
@@ -177,36 +192,36 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 #pragma unroll
     for (int j = 0; j < kTJ; ++j) *reinterpret_cast<uint4*>(lds + buf * kPTokBytes + tdst[j]) = tq[j];
   };
-  uint4 wq[kWRing][4];
-  auto load_weights = [&](int slot, int s) {
+  uint4 w0[4], w1[4], w2[4];   // raw weights of steps s, s+1, s+2
+  auto load_weights = [&](uint4 (&w)[4], int s) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) wq[slot][a] = pf_ld16(wr, woff[a] + (uint32_t)(s * 64));
+    for (int a = 0; a < 4; ++a) w[a] = pf_ld16(wr, woff[a] + (uint32_t)(s * 64));
   };
 
   // ---- prologue: weights of steps 0..2 in flight, tokens of step 0 in LDS, of step 1 in flight
-#pragma unroll
-  for (int s = 0; s < kWRing; ++s) load_weights(s, s);
+  load_weights(w0, 0);
+  load_weights(w1, 1);
+  load_weights(w2, 2);
   load_tokens(0);
   store_tokens(0);
   load_tokens(1);
   v8i aop[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) aop[a] = int4x32_to_e4m3(wq[0][a]);
-  __syncthreads();
+  for (int a = 0; a < 4; ++a) aop[a] = int4x32_to_e4m3(w0[a]);
+  lds_barrier();
 
-  // One k-step; SLOT = s % kWRing is a constant so that the weight ring stays in
-  // registers. The token blocks are walked with the next block's operand read ahead;
-  // into each block's 4 MFMAs go one token store (step s+1) or one token load (step s+2),
-  // one or two of the 16 words of the step s+1 weight conversion, and in the first 4 a
-  // weight load of step s+3; scheduling barriers keep the compiler from hoisting every
-  // LDS read to the top.
-  auto kstep = [&](int s, auto slot_tag) {
-    constexpr int SLOT = decltype(slot_tag)::value;
-    constexpr int NSLOT = (SLOT + 1) % kWRing;
+  // One k-step per iteration (a single loop body keeps every accumulator in place; the
+  // weight ring rotates by register copies at the end of the step). The token blocks are
+  // walked with the next block's operand read ahead; into each block's 4 MFMAs go one
+  // token store (step s+1) or one token load (step s+2), one or two of the 16 words of
+  // the step s+1 weight conversion, and in the first 4 a weight load of step s+3;
+  // scheduling barriers keep the compiler from hoisting every LDS read to the top.
+  for (int s = 0; s < steps; ++s) {
     const int cur = s & 1;
     const uint8_t* T = lds + cur * kPTokBytes;
     uint8_t* Tn = lds + (cur ^ 1) * kPTokBytes;
     v8i anext[4];
+    uint4 w3[4];
     v8i bcur = operand_from(*reinterpret_cast<const uint4*>(T + rd0), *reinterpret_cast<const uint4*>(T + rd1));
 #pragma unroll
     for (int bb = 0; bb < kTB; ++bb) {
@@ -221,37 +236,38 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
         *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                     // step s+1
       else
         tq[j] = pf_ld16(tr, toff[j] + (uint32_t)((s + 2) * 128));             // step s+2
-      if (bb < 4) wq[SLOT][bb] = pf_ld16(wr, woff[bb] + (uint32_t)((s + kWRing) * 64));
+      if (bb < 4) w3[bb] = pf_ld16(wr, woff[bb] + (uint32_t)((s + 3) * 64));
 #pragma unroll
       for (int wi = bb; wi < 16; wi += kTB) {
         const int a = wi >> 2, tw = wi & 3;
-        const uint32_t w = tw == 0 ? wq[NSLOT][a].x : tw == 1 ? wq[NSLOT][a].y : tw == 2 ? wq[NSLOT][a].z
-                                                                                         : wq[NSLOT][a].w;
-        anext[a][2 * tw] = (int)e4m3_of_nibbles(w & 0x07070707u, (w >> 3) & 0x01010101u);
-        anext[a][2 * tw + 1] = (int)e4m3_of_nibbles((w >> 4) & 0x07070707u, (w >> 7) & 0x01010101u);
+        const uint32_t w = tw == 0 ? w1[a].x : tw == 1 ? w1[a].y : tw == 2 ? w1[a].z : w1[a].w;
+        uint32_t lo, hi;
+        int4x8_to_e4m3(w, lo, hi);
+        anext[a][2 * tw] = (int)lo;
+        anext[a][2 * tw + 1] = (int)hi;
       }
       __builtin_amdgcn_sched_barrier(0);
       if (bb < kTB - 1) bcur = bnext;
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) aop[a] = anext[a];
-    __syncthreads();
-  };
-  using S0 = std::integral_constant<int, 0>;
-  using S1 = std::integral_constant<int, 1>;
-  using S2 = std::integral_constant<int, 2>;
-  static_assert(kWRing == 3, "the loop below is unrolled by the ring size");
-  int s = 0;
-  for (; s + 3 <= steps; s += 3) {
-    kstep(s, S0{});
-    kstep(s + 1, S1{});
-    kstep(s + 2, S2{});
+    for (int a = 0; a < 4; ++a) { aop[a] = anext[a]; w1[a] = w2[a]; w2[a] = w3[a]; }
+    lds_barrier();
   }
-  if (s < steps) kstep(s, S0{});
-  if (s + 1 < steps) kstep(s + 1, S1{});
 
-  // ---- epilogue: lane holds weight rows 4g..4g+3 of each block, token column i
+  // ---- epilogue: lane holds weight rows 4g..4g+3 of each block, token column i. Every
+  // value it reads is gathered before its first store (the byte stores may alias any
+  // load), so the loads overlap instead of each waiting behind the stores before it.
   const float* ws = p.w_scale + (size_t)o.e * p.Nw;
+  const int lim = GATEUP ? p.n_out : p.Nw;
+  int nbs[4];
+  float4 sc[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    // gate|up: a = 0, 1 gate scales of channel nbs[a], a = 2, 3 the up scales of nbs[a - 2]
+    nbs[a] = GATEUP ? n0 + 32 * wave + 16 * (a & 1) + 4 * g : n0 + 64 * wave + 16 * a + 4 * g;
+    const int nl = nbs[a] < lim ? nbs[a] : 0;
+    sc[a] = *reinterpret_cast<const float4*>(ws + (GATEUP && a >= 2 ? p.n_out : 0) + nl);
+  }
 #pragma unroll
   for (int bb = 0; bb < kTB; ++bb) {
     const int rt = 16 * bb + i;                              // row within the tile
@@ -260,17 +276,16 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     if (GATEUP) {
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const int nb = n0 + 32 * wave + 16 * a + 4 * g;      // channel
+        const int nb = nbs[a];                               // channel
         if (nb >= p.n_out) continue;
-        const float4 sg = *reinterpret_cast<const float4*>(ws + nb);
-        const float4 su = *reinterpret_cast<const float4*>(ws + p.n_out + nb);
-        const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+        const float sgv[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
+        const float suv[4] = {sc[a + 2].x, sc[a + 2].y, sc[a + 2].z, sc[a + 2].w};
         float gv[4], uv[4], av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           gv[v] = acc[bb][a][v] * p.s_act * sgv[v];
           uv[v] = acc[bb][a + 2][v] * p.s_act * suv[v];
-          av[v] = act_fn(gv[v], p.act_fn) * uv[v] / p.s_a;
+          av[v] = div_rn(act_fast<ACT>(gv[v]) * uv[v], p.s_a, p.inv_s_a);
         }
         *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
         if (p.dbg) {
@@ -282,14 +297,13 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     } else {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
-        const int nb = n0 + 64 * wave + 16 * a + 4 * g;
+        const int nb = nbs[a];
         if (nb >= p.Nw) continue;
-        const float4 sw = *reinterpret_cast<const float4*>(ws + nb);
         float4 out;
-        out.x = acc[bb][a][0] * p.s_act * sw.x;
-        out.y = acc[bb][a][1] * p.s_act * sw.y;
-        out.z = acc[bb][a][2] * p.s_act * sw.z;
-        out.w = acc[bb][a][3] * p.s_act * sw.w;
+        out.x = acc[bb][a][0] * p.s_act * sc[a].x;
+        out.y = acc[bb][a][1] * p.s_act * sc[a].y;
+        out.z = acc[bb][a][2] * p.s_act * sc[a].z;
+        out.w = acc[bb][a][3] * p.s_act * sc[a].w;
         *reinterpret_cast<float4*>(p.partial + (size_t)r * p.n_out + nb) = out;
       }
     }
@@ -298,17 +312,19 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 
 bool prefill_available() { return true; }
 
-size_t prefill_gemm2_partial_bytes(int T, int H) { return (size_t)2 * T * H * sizeof(float); }
-
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   // every expert's rows split into tiles of kPM; the count of tiles is at most P/kPM + E
   const int mtiles_upper = (p.P + kPM - 1) / kPM + p.E;
   const int ntiles = gateup ? (p.n_out + kPN / 2 - 1) / (kPN / 2) : (p.Nw + kPN - 1) / kPN;
   const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles);
-  if (gateup)
-    hipLaunchKernelGGL(moe_prefill_kernel<true>, dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+  if (!gateup)
+    hipLaunchKernelGGL((moe_prefill_kernel<false, 0>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+  else if (p.act_fn == 0)
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 0>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+  else if (p.act_fn == 1)
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 1>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
   else
-    hipLaunchKernelGGL(moe_prefill_kernel<false>, dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 2>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
 }
 
 }  // namespace w4a8
