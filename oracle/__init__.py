@@ -34,6 +34,7 @@ from .int4 import w4_quantize, w4_pack_codes, w4_unpack_codes, w4_pack, w4_dequa
 from .route import route_top2, route_sort
 from .moe import (ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH, activation, act_lipschitz,
                   quantize_static, static_scale, moe_forward, moe_reference_unquantized,
+                  expert_gate_up, expert_down,
                   moe_error_bound)
 from .block_fp8 import fp8_block_quantize, fp8_block_linear, fp8_block_linear_bruteforce
 
@@ -44,6 +45,6 @@ __all__ = [
     "route_top2", "route_sort",
     "ACT_SILU", "ACT_GELU_ERF", "ACT_GELU_TANH", "activation", "act_lipschitz",
     "quantize_static", "static_scale", "moe_forward", "moe_reference_unquantized",
-    "moe_error_bound",
+    "moe_error_bound", "expert_gate_up", "expert_down",
     "fp8_block_quantize", "fp8_block_linear", "fp8_block_linear_bruteforce",
 ]

@@ -94,6 +94,25 @@ def _int4_matmul(a_codes_f64, words, row_chunk=4096):
     return out
 
 
+def expert_gate_up(x_codes, words13, scales13, s_x):
+    """Step 4 for the rows of one expert: h = s_x * s_w13[n] * sum_k dec(x_hat[k]) q13[n, k].
+
+    x_codes: E4M3 codes [rows, H] of the tokens of these rows; words13 / scales13: any
+    subset of the expert's weight rows (the sums are independent per weight row).
+    """
+    acc = _int4_matmul(e4m3_decode(x_codes), words13)                     # exact
+    return acc * np.float64(s_x) * np.asarray(scales13, dtype=np.float64)[None, :]
+
+
+def expert_down(a_codes, words2, scales2, s_a):
+    """Step 7 for the rows of one expert: Y = s_a * s_w2[n] * sum_j dec(a_hat[j]) q2[n, j].
+
+    a_codes: E4M3 codes [rows, I]; words2 / scales2: any subset of the expert's rows.
+    """
+    acc2 = _int4_matmul(e4m3_decode(a_codes), words2)                      # exact
+    return acc2 * np.float64(s_a) * np.asarray(scales2, dtype=np.float64)[None, :]
+
+
 def moe_forward(x_bits, logits, s_x, w13, w2, act, s_a, out_f32=False, tokens=None,
                 E=None, a_codes_given=None):
     """Run the quantized layer (steps 1-8 of the module docstring).
@@ -144,14 +163,11 @@ def moe_forward(x_bits, logits, s_x, w13, w2, act, s_a, out_f32=False, tokens=No
             a = np.empty((rows.size, I))
             a_codes = np.empty((rows.size, I), dtype=np.uint8)
             y = np.empty((rows.size, H))
-        xe = e4m3_decode(x_codes[[code_of_token[int(t)] for t in token_of_row[sel]]])
-        acc = _int4_matmul(xe, words13)                                     # exact
-        he = acc * np.float64(s_x) * np.asarray(sc13, dtype=np.float64)[None, :]
+        he = expert_gate_up(x_codes[[code_of_token[int(t)] for t in token_of_row[sel]]], words13, sc13, s_x)
         ae = activation(he[:, :I], act) * he[:, I:]
         ce = quantize_static(ae.astype(np.float32), s_a)
         cd = ce if a_codes_given is None else np.asarray(a_codes_given, np.uint8)[rows[sel]]
-        acc2 = _int4_matmul(e4m3_decode(cd), words2)                        # exact
-        ye = acc2 * np.float64(s_a) * np.asarray(sc2, dtype=np.float64)[None, :]
+        ye = expert_down(cd, words2, sc2, s_a)
         h[sel], a[sel], a_codes[sel], y[sel] = he, ae, ce, ye
 
     out = np.empty((tokens.size, H))

@@ -175,3 +175,27 @@ def test_given_codes_feed_the_down_projection():
     others = np.arange(2 * cfg.T) != r
     assert np.array_equal(got["y"][others], base["y"][others])
     assert np.array_equal(got["h"], base["h"])
+
+
+def test_weight_row_subsets_match_full_tensor():
+    """The sampled full-size checks pack only some weight rows: quantization is per row, so
+    the rows regenerated by synth and packed alone equal those rows of the full packing,
+    and the per-expert steps on a row subset equal those columns of the full result."""
+    from oracle import expert_down, expert_gate_up
+    cfg = synth.custom_moe("rows", T=6, H=256, I=384, E=3, w_cfg=81, x_cfg=81)
+    x, logits, w13, w2 = _layer_inputs(cfg)
+    p13, p2 = w4_pack(w13), w4_pack(w2)
+    rows13 = np.array([0, 5, 127, 128, 383, 384, 600, 767])
+    rows2 = np.array([0, 1, 200, 255])
+    for e in range(cfg.E):
+        sub13 = w4_pack(synth.moe_weight_rows(cfg, "w13", e, rows13))
+        assert np.array_equal(sub13[0], p13[0][e][rows13]) and np.array_equal(sub13[1], p13[1][e][rows13])
+        sub2 = w4_pack(synth.moe_weight_rows(cfg, "w2", e, rows2))
+        assert np.array_equal(sub2[0], p2[0][e][rows2]) and np.array_equal(sub2[1], p2[1][e][rows2])
+    xc = quantize_static(bf16_to_f32(x), np.float32(0.01))
+    full = expert_gate_up(xc, p13[0][1], p13[1][1], np.float32(0.01))
+    part = expert_gate_up(xc, p13[0][1][rows13], p13[1][1][rows13], np.float32(0.01))
+    assert np.array_equal(part, full[:, rows13])
+    ac = quantize_static(np.random.default_rng(1).standard_normal((4, cfg.I)).astype(np.float32), np.float32(0.02))
+    full2 = expert_down(ac, p2[0][2], p2[1][2], np.float32(0.02))
+    assert np.array_equal(expert_down(ac, p2[0][2][rows2], p2[1][2][rows2], np.float32(0.02)), full2[:, rows2])
