@@ -55,16 +55,23 @@ def bf16_dev(torch, bits, dev):
 COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_prefill": "moe_prefill_grok_T32768.json"}
 
 
+def sources_sha256(paths):
+    """sha256 over the kernel's source files, in order (a changed kernel voids its counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()
+
+
 def counter_traffic(workload):
     """HBM bytes per gate|up launch from the committed rocprofv3 counters, or None when
-    they were taken on another workload or on a different kernel source."""
-    import hashlib
+    they were taken on another workload or on different kernel sources."""
     path = os.path.join(ROOT, "profiles", COUNTER_FILES.get(workload, "-"))
     if not os.path.exists(path):
         return None
     d = json.load(open(path))
-    src = open(os.path.join(ROOT, d["source"]), "rb").read()
-    if d.get("workload") != workload or hashlib.sha256(src).hexdigest() != d["source_sha256"]:
+    if d.get("workload") != workload or sources_sha256(d["sources"]) != d["sources_sha256"]:
         return None
     return int(d["traffic_bytes_per_launch"])
 
