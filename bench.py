@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--workload", default="mixtral_decode", choices=sorted(synth.MOE_CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-gemv", action="store_true", help="skip timing the block-FP8 GEMVs")
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="with the default decode workload, skip the prefill layer's line")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -111,14 +113,18 @@ def cpu_baseline(cfg, s_x, s_a, ids, max_tokens=32):
     toks = np.array([t for t, p in enumerate(pairs) if p == best], dtype=np.int64)[:max_tokens]
     packed13 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w13", e)) for e in best}
     packed2 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w2", e)) for e in best}
-    t0 = time.perf_counter()
-    oracle.moe_forward(x, logits, s_x, lambda e: packed13[e], lambda e: packed2[e], cfg.act, s_a, cfg.out_f32,
-                       tokens=toks, E=cfg.E)
-    dt = time.perf_counter() - t0
-    return {"value": float(len(toks) / dt), "unit": "tokens/s",
+    # the same forward repeated until about 10 s of host time (at most 8 runs)
+    runs, dt = 0, 0.0
+    while runs < 8 and dt < 10.0:
+        t0 = time.perf_counter()
+        oracle.moe_forward(x, logits, s_x, lambda e: packed13[e], lambda e: packed2[e], cfg.act, s_a, cfg.out_f32,
+                           tokens=toks, E=cfg.E)
+        dt += time.perf_counter() - t0
+        runs += 1
+    return {"value": float(runs * len(toks) / dt), "unit": "tokens/s",
             "cores": int(max(1, blas_threads)), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} tokens (routed to experts {best[0]} and {best[1]}), "
-                      f"full oracle forward (fp64, int4 unpack, exact sums); {dt:.2f} s"}
+                      f"full oracle forward (fp64, int4 unpack, exact sums), {runs} runs, {dt:.2f} s"}
 
 
 def bench_block_gemv(torch, W, dev, reps=16, iters=50):
@@ -148,16 +154,9 @@ def bench_block_gemv(torch, W, dev, reps=16, iters=50):
     return out
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the layer on one GPU's share); "
-              "--gpus above 1 is not supported.", file=sys.stderr)
-        sys.exit(2)
-    import torch
-    import w4a8_moe_amd as W
-
-    cfg = synth.MOE_CONFIGS[args.workload]
+def measure_layer(torch, W, cfg, steps, warmup):
+    """One workload: pack, graph-captured steps, the timed region, per-call durations.
+    Returns the JSON fields of the workload and the routing ids (for the CPU baseline)."""
     dev = torch.device("cuda:0")
     s_x, s_a = static_scales(cfg.name)
     T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
@@ -220,7 +219,7 @@ def main():
         with torch.cuda.graph(g):
             step(c)
         graphs.append(g)
-    for i in range(args.warmup):
+    for i in range(warmup):
         graphs[i % copies].replay()
     torch.cuda.synchronize()
     graphs[0].replay()
@@ -231,17 +230,17 @@ def main():
     # ---- timed region: K steps, wall clock between two synchronizations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         graphs[i % copies].replay()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
+    ms_per_step = elapsed * 1e3 / steps
 
     # ---- per-call duration: back-to-back launches of one call between two HIP events on
     #      the stream the library launches on
     st = torch.cuda.current_stream()
 
-    def per_launch_us(fn, n=max(20, args.steps)):
+    def per_launch_us(fn, n=max(20, steps)):
         for i in range(3):
             fn(i)
         ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -278,8 +277,8 @@ def main():
         "value": round(T / (ms_per_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
@@ -295,6 +294,28 @@ def main():
         "roofline": roofline,
         "w4_pack": {"ms": round(pack_ms, 3), "GB/s": round(pack_bytes / pack_ms / 1e6, 1)},
     }
+    return result, ids
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the layer on one GPU's share); "
+              "--gpus above 1 is not supported.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import w4a8_moe_amd as W
+
+    cfg = synth.MOE_CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    result, ids = measure_layer(torch, W, cfg, args.steps, args.warmup)
+    if args.workload == "mixtral_decode" and not args.no_prefill:
+        # the metric's second half: the Grok-1-shaped prefill layer, bound by the matrix cores
+        torch.cuda.empty_cache()
+        pf, _ = measure_layer(torch, W, synth.GROK_PREFILL, min(args.steps, 10), min(args.warmup, 2))
+        result["prefill"] = {k: pf[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
+                                                 "layer_mfma_frac", "calls_us", "roofline")}
+        torch.cuda.empty_cache()
     if args.copy_ref:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -305,7 +326,7 @@ def main():
     if not args.no_block_gemv:
         result["block_fp8_gemv"] = bench_block_gemv(torch, W, dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, s_x, s_a, ids)
+        result["cpu_baseline"] = cpu_baseline(cfg, *static_scales(cfg.name), ids)
     print(json.dumps(result), flush=True)
 
 
