@@ -71,9 +71,16 @@ __device__ __forceinline__ uint32_t e4m3_of_nibbles(uint32_t sel, uint32_t sgn) 
 
 // One packed word (byte b: element b in the low nibble, element 4+b in the high nibble)
 // -> E4M3 codes of elements 0..3 (lo) and 4..7 (hi).
-__device__ __forceinline__ void int4x8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t& hi) {
-  lo = e4m3_of_nibbles(w & 0x07070707u, (w >> 1) & 0x04040404u);
-  hi = e4m3_of_nibbles((w >> 4) & 0x07070707u, (w >> 5) & 0x04040404u);
+__device__ __forceinline__ uint32_t e4m3_of_nibbles_sel(uint32_t sel, uint32_t selsgn) {
+  const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
+  const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
+  return __builtin_amdgcn_perm(neg, pos, selsgn);
+}
+__device__ __forceinline__ void int4x8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t& hi, uint32_t m4 = 0x04040404u,
+                                               uint32_t id = 0x03020100u) {
+  const uint32_t w4 = w >> 4;
+  lo = e4m3_of_nibbles_sel(w & 0x07070707u, ((w >> 1) & m4) | id);
+  hi = e4m3_of_nibbles_sel(w4 & 0x07070707u, ((w4 >> 1) & m4) | id);
 }
 
 __device__ __forceinline__ v8i int4x32_to_e4m3(uint4 q) {
@@ -192,7 +199,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 #pragma unroll
     for (int j = 0; j < kTJ; ++j) *reinterpret_cast<uint4*>(lds + buf * kPTokBytes + tdst[j]) = tq[j];
   };
-  uint4 w0[4], w1[4], w2[4];   // raw weights of steps s, s+1, s+2
+  uint4 w0[4], w1[4];          // raw weights of steps s and s+1
   auto load_weights = [&](uint4 (&w)[4], int s) {
 #pragma unroll
     for (int a = 0; a < 4; ++a) w[a] = pf_ld16(wr, woff[a] + (uint32_t)(s * 64));
@@ -201,7 +208,6 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   // ---- prologue: weights of steps 0..2 in flight, tokens of step 0 in LDS, of step 1 in flight
   load_weights(w0, 0);
   load_weights(w1, 1);
-  load_weights(w2, 2);
   load_tokens(0);
   store_tokens(0);
   load_tokens(1);
@@ -210,18 +216,21 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   for (int a = 0; a < 4; ++a) aop[a] = int4x32_to_e4m3(w0[a]);
   lds_barrier();
 
-  // One k-step per iteration (a single loop body keeps every accumulator in place; the
-  // weight ring rotates by register copies at the end of the step). The token blocks are
-  // walked with the next block's operand read ahead; into each block's 4 MFMAs go one
-  // token store (step s+1) or one token load (step s+2), one or two of the 16 words of
-  // the step s+1 weight conversion, and in the first 4 a weight load of step s+3;
-  // scheduling barriers keep the compiler from hoisting every LDS read to the top.
+  // One k-step per iteration (a single loop body keeps every accumulator in place). The
+  // token blocks are walked with the next block's operand read ahead; into each block's 4
+  // MFMAs go one token store (step s+1) or one token load (step s+2) and one or two of the
+  // 16 words of the step s+1 weight conversion; a weight block's raw registers are
+  // reloaded with step s+2 as soon as its last word is converted. Scheduling barriers keep
+  // the compiler from hoisting every LDS read to the top.
+  // the two byte masks of the conversion live in registers, so that mask-and-merge is one
+  // 3-input bit operation
+  uint32_t km4 = 0x04040404u, kid = 0x03020100u;
+  asm volatile("" : "+v"(km4), "+v"(kid));
   for (int s = 0; s < steps; ++s) {
     const int cur = s & 1;
     const uint8_t* T = lds + cur * kPTokBytes;
     uint8_t* Tn = lds + (cur ^ 1) * kPTokBytes;
     v8i anext[4];
-    uint4 w3[4];
     v8i bcur = operand_from(*reinterpret_cast<const uint4*>(T + rd0), *reinterpret_cast<const uint4*>(T + rd1));
 #pragma unroll
     for (int bb = 0; bb < kTB; ++bb) {
@@ -236,21 +245,29 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
         *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                     // step s+1
       else
         tq[j] = pf_ld16(tr, toff[j] + (uint32_t)((s + 2) * 128));             // step s+2
-      if (bb < 4) w3[bb] = pf_ld16(wr, woff[bb] + (uint32_t)((s + 3) * 64));
 #pragma unroll
       for (int wi = bb; wi < 16; wi += kTB) {
         const int a = wi >> 2, tw = wi & 3;
         const uint32_t w = tw == 0 ? w1[a].x : tw == 1 ? w1[a].y : tw == 2 ? w1[a].z : w1[a].w;
         uint32_t lo, hi;
-        int4x8_to_e4m3(w, lo, hi);
+        int4x8_to_e4m3(w, lo, hi, km4, kid);
         anext[a][2 * tw] = (int)lo;
         anext[a][2 * tw + 1] = (int)hi;
       }
+      // words wi are converted at bb = wi % kTB: block a's last word (wi = 4 a + 3) goes at
+      // bb = 3 for a = 0 and 3 (wi = 15 -> bb 3), bb = 7 for a = 1, bb = 11 for a = 2
+      static_assert(kTB == 12, "the reload points below follow the conversion order for 12 blocks");
+      if (bb == 3) {
+        w1[0] = pf_ld16(wr, woff[0] + (uint32_t)((s + 2) * 64));
+        w1[3] = pf_ld16(wr, woff[3] + (uint32_t)((s + 2) * 64));
+      }
+      if (bb == 7) w1[1] = pf_ld16(wr, woff[1] + (uint32_t)((s + 2) * 64));
+      if (bb == 11) w1[2] = pf_ld16(wr, woff[2] + (uint32_t)((s + 2) * 64));
       __builtin_amdgcn_sched_barrier(0);
       if (bb < kTB - 1) bcur = bnext;
     }
 #pragma unroll
-    for (int a = 0; a < 4; ++a) { aop[a] = anext[a]; w1[a] = w2[a]; w2[a] = w3[a]; }
+    for (int a = 0; a < 4; ++a) aop[a] = anext[a];
     lds_barrier();
   }
 
