@@ -17,13 +17,13 @@
 // with the sum of |products|, about six times larger with the offset: that failed the
 // output tolerance.)
 //
-// Tile. A workgroup computes 192 sorted rows (tokens of one expert) x 256 weight rows,
+// Tile. A workgroup computes 256 sorted rows (tokens of one expert) x 256 weight rows,
 // K in steps of 128, with 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against
-// all 192 tokens (12 blocks), so its int4 codes go from global memory straight into its
+// all 256 tokens (16 blocks), so its int4 codes go from global memory straight into its
 // own registers, are converted there and are used as MFMA operands without an LDS round
 // trip. For
 // gate|up the 64 rows are 32 gate channels and the 32 matching up channels, so
-// act(gate) * up is formed in registers. Only the token tile (192 x 128 E4M3 codes per
+// act(gate) * up is formed in registers. Only the token tile (256 x 128 E4M3 codes per
 // k-step, gathered through sorted_pair for gate|up) is shared through LDS, double
 // buffered, in MFMA operand order with an XOR swizzle that keeps both the staging writes
 // and the operand reads free of bank conflicts.
@@ -45,7 +45,7 @@
 
 namespace w4a8 {
 
-constexpr int kTB = 12;           // token blocks of 16 rows per tile
+constexpr int kTB = 16;           // token blocks of 16 rows per tile
 constexpr int kPM = 16 * kTB;     // sorted rows per tile
 constexpr int kPN = 256;          // weight rows per tile
 constexpr int kPThreads = 256;    // 4 waves, 64 weight rows each
@@ -254,15 +254,9 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
         anext[a][2 * tw] = (int)lo;
         anext[a][2 * tw + 1] = (int)hi;
       }
-      // words wi are converted at bb = wi % kTB: block a's last word (wi = 4 a + 3) goes at
-      // bb = 3 for a = 0 and 3 (wi = 15 -> bb 3), bb = 7 for a = 1, bb = 11 for a = 2
-      static_assert(kTB == 12, "the reload points below follow the conversion order for 12 blocks");
-      if (bb == 3) {
-        w1[0] = pf_ld16(wr, woff[0] + (uint32_t)((s + 2) * 64));
-        w1[3] = pf_ld16(wr, woff[3] + (uint32_t)((s + 2) * 64));
-      }
-      if (bb == 7) w1[1] = pf_ld16(wr, woff[1] + (uint32_t)((s + 2) * 64));
-      if (bb == 11) w1[2] = pf_ld16(wr, woff[2] + (uint32_t)((s + 2) * 64));
+      // words wi are converted at bb = wi (16 blocks): block a's last word goes at bb = 4 a + 3
+      static_assert(kTB == 16, "the reload points below follow the conversion order for 16 blocks");
+      if ((bb & 3) == 3) w1[bb >> 2] = pf_ld16(wr, woff[bb >> 2] + (uint32_t)((s + 2) * 64));
       __builtin_amdgcn_sched_barrier(0);
       if (bb < kTB - 1) bcur = bnext;
     }
