@@ -274,48 +274,52 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   float4 sc[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    // gate|up: a = 0, 1 gate scales of channel nbs[a], a = 2, 3 the up scales of nbs[a - 2]
+    // gate|up: a = 0, 1 gate scales of channel nbs[a], a = 2, 3 the up scales of nbs[a - 2];
+    // each folded with the activation's static scale once
     nbs[a] = GATEUP ? n0 + 32 * wave + 16 * (a & 1) + 4 * g : n0 + 64 * wave + 16 * a + 4 * g;
     const int nl = nbs[a] < lim ? nbs[a] : 0;
-    sc[a] = *reinterpret_cast<const float4*>(ws + (GATEUP && a >= 2 ? p.n_out : 0) + nl);
+    const float4 w4 = *reinterpret_cast<const float4*>(ws + (GATEUP && a >= 2 ? p.n_out : 0) + nl);
+    sc[a] = make_float4(w4.x * p.s_act, w4.y * p.s_act, w4.z * p.s_act, w4.w * p.s_act);
   }
+  // Values are computed for every (row, channel) of the lane, uniformly; only the stores
+  // are guarded (rows and channels past the tile's valid range hold zero sums).
 #pragma unroll
   for (int bb = 0; bb < kTB; ++bb) {
     const int rt = 16 * bb + i;                              // row within the tile
-    if (rt >= rows) continue;
-    const int r = o.seg0 + o.m0 + rt;                        // sorted row
+    const bool row_ok = rt < rows;
+    const size_t r = (size_t)(o.seg0 + o.m0 + (row_ok ? rt : 0));   // sorted row
     if (GATEUP) {
+      uint8_t* arow = p.a_out + r * p.n_out;
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int nb = nbs[a];                               // channel
-        if (nb >= p.n_out) continue;
         const float sgv[4] = {sc[a].x, sc[a].y, sc[a].z, sc[a].w};
         const float suv[4] = {sc[a + 2].x, sc[a + 2].y, sc[a + 2].z, sc[a + 2].w};
         float gv[4], uv[4], av[4];
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          gv[v] = acc[bb][a][v] * p.s_act * sgv[v];
-          uv[v] = acc[bb][a + 2][v] * p.s_act * suv[v];
+          gv[v] = acc[bb][a][v] * sgv[v];
+          uv[v] = acc[bb][a + 2][v] * suv[v];
           av[v] = div_rn(act_fast<ACT>(gv[v]) * uv[v], p.s_a, p.inv_s_a);
         }
-        *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
-        if (p.dbg) {
-          float* d = p.dbg + (size_t)r * 2 * p.n_out;
-          *reinterpret_cast<float4*>(d + nb) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-          *reinterpret_cast<float4*>(d + p.n_out + nb) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+        const uint32_t codes = pack4_e4m3(av[0], av[1], av[2], av[3]);
+        if (row_ok && nb < p.n_out) {
+          *reinterpret_cast<uint32_t*>(arow + nb) = codes;
+          if (p.dbg) {
+            float* d = p.dbg + r * 2 * p.n_out;
+            *reinterpret_cast<float4*>(d + nb) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+            *reinterpret_cast<float4*>(d + p.n_out + nb) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+          }
         }
       }
     } else {
+      float* prow = p.partial + r * p.n_out;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int nb = nbs[a];
-        if (nb >= p.Nw) continue;
-        float4 out;
-        out.x = acc[bb][a][0] * p.s_act * sc[a].x;
-        out.y = acc[bb][a][1] * p.s_act * sc[a].y;
-        out.z = acc[bb][a][2] * p.s_act * sc[a].z;
-        out.w = acc[bb][a][3] * p.s_act * sc[a].w;
-        *reinterpret_cast<float4*>(p.partial + (size_t)r * p.n_out + nb) = out;
+        const float4 out = make_float4(acc[bb][a][0] * sc[a].x, acc[bb][a][1] * sc[a].y,
+                                       acc[bb][a][2] * sc[a].z, acc[bb][a][3] * sc[a].w);
+        if (row_ok && nb < p.Nw) *reinterpret_cast<float4*>(prow + nb) = out;
       }
     }
   }
