@@ -101,6 +101,22 @@ int32_t w4_pack(const uint16_t* w_bf16, int32_t E, int32_t N, int32_t K,
                 int32_t* packed, float* scale, void* stream);
 
 /*
+ * w4_tile -- the tiled layout the MoE GEMMs read their int4 weights in, made once at load
+ * time from w4_pack's output (a byte permutation: values and nibble order unchanged).
+ *
+ *   packed  [E][N][K/8] int32 from w4_pack (rows of K/2 bytes)
+ *   tiled   [E][N/16][K/128][256] int32 (output, the same byte count): per expert, tiles
+ *           of 16 rows x 128 K (1 KB), the k-steps of one 16-row block consecutive; in
+ *           tile (nb, ks) the 16 bytes at offset 16 * (i + 16 g), 0 <= i < 16, 0 <= g < 4,
+ *           are bytes 64 ks + 16 g .. 64 ks + 16 g + 15 of row 16 nb + i of `packed`.
+ * One 16-byte load per lane of a 64-lane wave then fetches a whole contiguous tile in the
+ * order the matrix instructions take it (row i, K = 128 ks + 32 g .. +32).
+ * Requires E >= 1, N % 16 == 0, K % 128 == 0 (N >= 16, K >= 128), E*N < 2^31, both
+ * pointers 16-byte aligned, and the two buffers not overlapping (W4A8_ERR_ARG).
+ */
+int32_t w4_tile(const int32_t* packed, int32_t E, int32_t N, int32_t K, int32_t* tiled, void* stream);
+
+/*
  * fp8_quant_static -- tensor-wise static FP8 quantization ("tensor-wise FP8
  * quantization", Highlights of the page "[AMD][Quantization] Add int4fp8_moe online
  * quantization on ROCm"; activation_scheme static, page "ROCm: enable ...").
@@ -141,7 +157,8 @@ int32_t moe_route_sort(const float* logits, int32_t T, int32_t E,
  *   x        [T][H]  x_dtype W4A8_DT_BF16 (quantized here with s_x exactly as
  *                    fp8_quant_static does) or W4A8_DT_E4M3 (already quantized codes)
  *   s_x      static scale of x (finite, > 0)
- *   w13      [E][2I][H/8] int32 from w4_pack: rows [0,I) gate, rows [I,2I) up
+ *   w13      [E][2I/16][H/128][256] int32 from w4_tile (of w4_pack's [E][2I][H/8]):
+ *            rows [0,I) gate, rows [I,2I) up
  *   s_w13    [E][2I] fp32 from w4_pack
  *   offsets, sorted_pair from moe_route_sort
  *   act      W4A8_ACT_*;  s_a  static scale of the intermediate (finite, > 0)
@@ -149,8 +166,9 @@ int32_t moe_route_sort(const float* logits, int32_t T, int32_t E,
  *              h = s_x * s_w13[e][n] * sum_k x_hat[t][k] * q13[e][n][k]   (t = sorted_pair[r]/2)
  *              a_fp8[r][n] = e4m3(fp32(act(h[n]) * h[I+n]) / s_a)
  *   gateup_dbg [2T][2I] fp32 (out, optional, NULL to skip): h per sorted row
- * Accuracy: up to 64 tokens (w4a8_moe_kernel) the sums are exact products added in
- * fp32; above it the fp8 matrix instruction adds each 128-long block of products with
+ * Accuracy: up to 64 tokens (w4a8_moe_kernel) the products are exact and added in fp32
+ * (each code enters as q + 8; 8 times the fp32 sum of the row of x_hat is taken off after
+ * the sum, so h carries about twice the rounding of a plain fp32 sum); above it the fp8 matrix instruction adds each 128-long block of products with
  * about 14 bits below its largest product, so h carries a relative error of about
  * 1e-5 of its row's largest value, and a code of a_fp8 can then sit one step from the
  * one an exact h gives.
@@ -170,7 +188,8 @@ int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x,
  * passages as moe_gemm1_w4a8).
  *
  *   a_fp8   [2T][I] e4m3 from moe_gemm1_w4a8 (sorted rows);  s_a its static scale
- *   w2      [E][H][I/8] int32 from w4_pack;  s_w2 [E][H] fp32
+ *   w2      [E][H/16][I/128][256] int32 from w4_tile (of w4_pack's [E][H][I/8]);
+ *           s_w2 [E][H] fp32 from w4_pack
  *   offsets, pair_pos from moe_route_sort;  topk_w [T][2] from moe_route_sort
  *   out     [T][H] (out) out_dtype W4A8_DT_BF16 (round to nearest even) or W4A8_DT_F32:
  *             Y[r][n]  = s_a * s_w2[e][n] * sum_j a_hat[r][j] * q2[e][n][j]

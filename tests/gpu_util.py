@@ -123,3 +123,28 @@ def _assert_adjacent(c1, c2):
     mg, mr = cg & 0x7F, cr & 0x7F
     adjacent = ((cg >> 7) == (cr >> 7)) & (np.abs(mg - mr) == 1) | ((mg == 0) & (mr == 1)) | ((mr == 0) & (mg == 1))
     assert adjacent.all(), "a code flip is not between neighbouring codes"
+
+
+def tile_words(packed):
+    """The GEMMs' tiled weight layout, from its definition: int32 [E, N, K/8] -> [E, N/16,
+    K/128, 256] where 16-byte unit i + 16 g of tile (nb, ks) is bytes 64 ks + 16 g .. +16
+    of row 16 nb + i."""
+    packed = np.asarray(packed)
+    E, N, K8 = packed.shape
+    x = packed.reshape(E, N // 16, 16, K8 // 16, 4, 4)        # e, nb, i, ks, g, word
+    return np.ascontiguousarray(x.transpose(0, 1, 3, 4, 2, 5)).reshape(E, N // 16, K8 // 16, 256)
+
+
+def rows_of_tiled(tiled_e, rows):
+    """Rows (in w4_pack's row layout, int32 [len(rows), K/8]) of one expert's tiled words
+    [N/16, K/128, 256]."""
+    rows = np.asarray(rows)
+    if isinstance(tiled_e, np.ndarray):
+        t, nb, i = tiled_e, rows // 16, rows % 16
+    else:                                                       # a device tensor: gather there
+        t = tiled_e
+        nb, i = (torch().from_numpy(v).to(t.device) for v in (rows // 16, rows % 16))
+    NB, KT, _ = t.shape
+    x = t.reshape(NB, KT, 4, 16, 4)                             # nb, ks, g, i, word
+    got = x[nb, :, :, i, :].reshape(len(rows), KT * 16)
+    return got if isinstance(got, np.ndarray) else host(got)

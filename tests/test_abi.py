@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert set(names) == {"w4_pack", "fp8_quant_static", "moe_route_sort", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
+    assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
                           "fp8_block_quant", "fp8_block_linear", "w4a8_workspace_bytes", "w4a8_status_str",
                           "w4a8_moe_kernel"}
     for n in names:
@@ -34,6 +34,20 @@ def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert W.status_str(code) and W.status_str(code) != "unknown status"
     assert W.status_str(-99) == "unknown status"
+
+
+def test_w4_tile_validation(L):
+    B = A + (1 << 20)
+    assert L.w4_tile(None, 1, 16, 128, A, None) == W.ERR_NULL
+    assert L.w4_tile(A, 1, 16, 128, None, None) == W.ERR_NULL
+    assert L.w4_tile(A, 1, 24, 128, B, None) == W.ERR_SHAPE           # N % 16
+    assert L.w4_tile(A, 1, 16, 192, B, None) == W.ERR_SHAPE           # K % 128
+    assert L.w4_tile(A, 0, 16, 128, B, None) == W.ERR_SHAPE
+    assert L.w4_tile(A, 1, 0, 128, B, None) == W.ERR_SHAPE
+    assert L.w4_tile(U, 1, 16, 128, B, None) == W.ERR_ALIGN
+    assert L.w4_tile(A, 1, 16, 128, U, None) == W.ERR_ALIGN
+    assert L.w4_tile(A, 1, 16, 128, A, None) == W.ERR_ARG             # in place
+    assert L.w4_tile(A, 1, 16, 128, A + 512, None) == W.ERR_ARG       # overlapping
 
 
 def test_w4_pack_validation(L):

@@ -1,6 +1,6 @@
 """Parity of the HIP library (through the C ABI) with the CPU oracle on seeded inputs.
 
-Bit-exact: packing, scales, fp8 activation codes, routing ids, counts, offsets,
+Bit-exact: packing, the tiled weight layout, scales, fp8 activation codes, routing ids, counts, offsets,
 sorted_pair, pair_pos, block-FP8 codes and scales. Tolerances: topk_w 1e-6; gate|up
 1e-4 x row max; final outputs 1e-2 x max|ref| with at most 0.1% of elements above
 1e-3 x max|ref| (bf16 outputs against the oracle's bf16-rounded result).
@@ -12,7 +12,7 @@ import oracle
 import synth
 import w4a8_moe_amd as W
 from tests.gpu_util import (assert_codes_consistent, assert_final_close, assert_gateup_close, bf16_bits_to_f64,
-                            bf16_dev, f32_dev, host, same_codes, torch, u8_dev)
+                            bf16_dev, f32_dev, host, same_codes, tile_words, torch, u8_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,16 @@ def test_w4_pack_tiny_layer():
         packed, scale = W.w4_pack(bf16_dev(w))
         ref_p, ref_s = oracle.w4_pack(w)
         assert np.array_equal(host(scale), ref_s) and np.array_equal(host(packed), ref_p)
+
+
+@pytest.mark.parametrize("E,N,K", [(1, 16, 128), (3, 48, 384), (2, 272, 1152)])
+def test_w4_tile_bit_exact(E, N, K):
+    rng = np.random.default_rng(E * 7 + N + K)
+    packed = rng.integers(-2**31, 2**31, (E, N, K // 8), dtype=np.int64).astype(np.int32)
+    tiled = W.w4_tile(torch().from_numpy(packed).to("cuda"))
+    assert np.array_equal(host(tiled), tile_words(packed))
+    t2 = W.w4_pack(bf16_dev(synth.f32_to_bf16_bits(rng.standard_normal((E, N, K)).astype(np.float32))), tiled=True)
+    assert tuple(t2[0].shape) == (E, N // 16, K // 128, 256)
 
 
 # ------------------------------------------------------------------------ route + sort
@@ -118,6 +128,24 @@ def _oracle_scales(cfg, x, logits, p13, p2):
     return s_x, oracle.static_scale(np.max(np.abs(pre["a"])))
 
 
+def _check_final(cfg, x, logits, s_x, p13, p2, s_a, ref, a, out):
+    """The requantized codes are decided on the kernel's own gate|up, so a code at a rounding
+    boundary may differ from the oracle's (checked by assert_codes_consistent). The final
+    output is held to the full bar against the oracle's down projection and combine of the
+    kernel's codes, and to the 1e-2 bar against the oracle's end-to-end result."""
+    same = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32, a_codes_given=host(a))
+    if cfg.out_f32:
+        got, want, e2e = host(out), same["out"].astype(np.float32), ref["out"].astype(np.float32)
+    else:
+        got = bf16_bits_to_f64(host(out))
+        want, e2e = bf16_bits_to_f64(same["out_rounded"]), bf16_bits_to_f64(ref["out_rounded"])
+    assert_final_close(got, want)
+    m = np.max(np.abs(e2e))
+    d = np.abs(np.asarray(got, np.float64) - e2e)
+    print(f"end to end: max err {d.max() / m:.3g} x max|ref|, {np.mean(d > 1e-3 * m):.4%} above 1e-3", flush=True)
+    assert d.max() <= 1e-2 * m
+
+
 LAYER_CASES = [
     synth.TINY,
     synth.custom_moe("ragged_k", T=32, H=640, I=4736, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=201,
@@ -143,22 +171,20 @@ def test_moe_layer_parity(cfg):
     gw2, gs2 = W.w4_pack(bf16_dev(w2))
     assert np.array_equal(host(gw13), p13[0]) and np.array_equal(host(gs13), p13[1])
     assert np.array_equal(host(gw2), p2[0]) and np.array_equal(host(gs2), p2[1])
+    gw13, gw2 = W.w4_tile(gw13), W.w4_tile(gw2)
     r = W.moe_route_sort(f32_dev(logits))
     assert np.array_equal(host(r["sorted_pair"]), ref["sorted_pair"])
     xd = bf16_dev(x)
     a, h = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a, debug=True)
     assert_gateup_close(host(h), ref["h"])
-    assert_codes_consistent(host(a), ref["a_codes"], host(h), cfg.act, s_a, cfg.I)
+    assert_codes_consistent(host(a), ref["a_codes"], host(h), cfg.act, s_a, cfg.I, a_ref=ref["a"])
     # the pre-quantized x path gives identical bytes
     xq = W.fp8_quant_static(xd, s_x)
     a2 = W.moe_gemm1_w4a8(xq, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a)
     assert torch().equal(a, a2)
     out = W.moe_gemm2_w4a8(a, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"],
                            "f32" if cfg.out_f32 else "bf16")
-    if cfg.out_f32:
-        assert_final_close(host(out), ref["out"].astype(np.float32))
-    else:
-        assert_final_close(bf16_bits_to_f64(host(out)), bf16_bits_to_f64(ref["out_rounded"]))
+    _check_final(cfg, x, logits, s_x, p13, p2, s_a, ref, a, out)
     # determinism: a second run is byte-identical
     a3 = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a)
     out3 = W.moe_gemm2_w4a8(a3, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"],
@@ -184,10 +210,7 @@ PREFILL_CASES = [
 
 @pytest.mark.parametrize("cfg", PREFILL_CASES, ids=[c.name for c in PREFILL_CASES])
 def test_moe_prefill_parity(cfg):
-    """The tiled path. gate|up to the 1e-4 bar; the requantized codes are decided on the
-    kernel's own gate|up (checked against the oracle's epilogue), and the final output is
-    held to the full bar against the oracle's down projection and combine of those codes,
-    and to the 1e-2 bar against the oracle's end-to-end result."""
+    """The tiled path: gate|up to the 1e-4 bar, codes and final output as in the layer test."""
     x = synth.activations(cfg)
     logits = synth.router_logits(cfg)
     w13 = synth.moe_weights(cfg, "w13")
@@ -195,8 +218,8 @@ def test_moe_prefill_parity(cfg):
     p13, p2 = oracle.w4_pack(w13), oracle.w4_pack(w2)
     s_x, s_a = _oracle_scales(cfg, x, logits, p13, p2)
     ref = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32)
-    gw13, gs13 = W.w4_pack(bf16_dev(w13))
-    gw2, gs2 = W.w4_pack(bf16_dev(w2))
+    gw13, gs13 = W.w4_pack(bf16_dev(w13), tiled=True)
+    gw2, gs2 = W.w4_pack(bf16_dev(w2), tiled=True)
     r = W.moe_route_sort(f32_dev(logits))
     assert np.array_equal(host(r["offsets"]), ref["offsets"])
     print(f"{cfg.name}: rows per expert {np.diff(ref['offsets']).tolist()}", flush=True)
@@ -209,17 +232,7 @@ def test_moe_prefill_parity(cfg):
     assert torch().equal(a, a2)
     od = "f32" if cfg.out_f32 else "bf16"
     out = W.moe_gemm2_w4a8(a, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"], od)
-    same = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32, a_codes_given=host(a))
-    if cfg.out_f32:
-        got, want, e2e = host(out), same["out"].astype(np.float32), ref["out"].astype(np.float32)
-    else:
-        got = bf16_bits_to_f64(host(out))
-        want, e2e = bf16_bits_to_f64(same["out_rounded"]), bf16_bits_to_f64(ref["out_rounded"])
-    assert_final_close(got, want)
-    m = np.max(np.abs(e2e))
-    d = np.abs(np.asarray(got, np.float64) - e2e)
-    print(f"end to end: max err {d.max() / m:.3g} x max|ref|, {np.mean(d > 1e-3 * m):.4%} above 1e-3", flush=True)
-    assert d.max() <= 1e-2 * m
+    _check_final(cfg, x, logits, s_x, p13, p2, s_a, ref, a, out)
     a3 = W.moe_gemm1_w4a8(xd, s_x, gw13, gs13, r["offsets"], r["sorted_pair"], cfg.act, s_a)
     out3 = W.moe_gemm2_w4a8(a3, s_a, gw2, gs2, r["offsets"], r["pair_pos"], r["weights"], od)
     assert torch().equal(a, a3) and torch().equal(out, out3)
@@ -236,7 +249,7 @@ def test_integer_case_gate_up_bit_exact():
     x = synth.f32_to_bf16_bits(xi.astype(np.float32))
     w13 = synth.f32_to_bf16_bits(w13i.astype(np.float32))
     logits = rng.standard_normal((T, E)).astype(np.float32)
-    gw13, gs13 = W.w4_pack(bf16_dev(w13))
+    gw13, gs13 = W.w4_pack(bf16_dev(w13), tiled=True)
     assert np.all(host(gs13) == 1.0)
     r = W.moe_route_sort(f32_dev(logits))
     a, h = W.moe_gemm1_w4a8(bf16_dev(x), 1.0, gw13, gs13, r["offsets"], r["sorted_pair"], W.ACT_SILU, 1.0,

@@ -17,8 +17,8 @@ import oracle
 import synth
 import w4a8_moe_amd as W
 from oracle.sample import prefill_token_subset
-from tests.gpu_util import (assert_final_close, bf16_bits_to_f64, bf16_dev, f32_dev, host, same_codes,
-                            static_scales, torch)
+from tests.gpu_util import (assert_final_close, bf16_bits_to_f64, bf16_dev, f32_dev, host, rows_of_tiled,
+                            same_codes, static_scales, torch)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -59,7 +59,7 @@ def _run_sampled(cfg, n_tokens, n_ch):
     gw = {}
     for which in ("w13", "w2"):
         wb = bf16_dev(synth.moe_weights(cfg, which))
-        gw[which] = W.w4_pack(wb)
+        gw[which] = W.w4_pack(wb, tiled=True)
         del wb
         torch().cuda.empty_cache()
     r = W.moe_route_sort(f32_dev(logits))
@@ -85,7 +85,7 @@ def _run_sampled(cfg, n_tokens, n_ch):
         sel = np.nonzero(expert_of == e)[0]
         r13 = np.concatenate([ch, I + ch])
         words13, sc13 = oracle.w4_pack(synth.moe_weight_rows(cfg, "w13", int(e), r13))
-        assert np.array_equal(host(gw["w13"][0][int(e)][torch().from_numpy(r13).to(a.device)]), words13)
+        assert np.array_equal(rows_of_tiled(gw["w13"][0][int(e)], r13), words13)
         assert np.array_equal(host(gw["w13"][1][int(e)][torch().from_numpy(r13).to(a.device)]), sc13)
         xc = oracle.quantize_static(oracle.bf16_to_f32(x[sp[rows[sel]] // 2]), s_x)
         h = oracle.expert_gate_up(xc, words13, sc13, s_x)                     # [sel, 2 n_ch]
@@ -103,7 +103,7 @@ def _run_sampled(cfg, n_tokens, n_ch):
         near += int(np.sum(~ok & (got >= lo - 1) & (got <= hi + 1)))
         total += got.size
         words2, sc2 = oracle.w4_pack(synth.moe_weight_rows(cfg, "w2", int(e), ch2))
-        assert np.array_equal(host(gw["w2"][0][int(e)][torch().from_numpy(ch2).to(a.device)]), words2)
+        assert np.array_equal(rows_of_tiled(gw["w2"][0][int(e)], ch2), words2)
         y[sel] = oracle.expert_down(a_rows[sel], words2, sc2, s_a)
     print(f"codes: {exact / total:.4%} equal the oracle's, {within / total:.4%} within reach of the 1e-4 row bar",
           flush=True)

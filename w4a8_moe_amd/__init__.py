@@ -33,6 +33,7 @@ _SZ = ctypes.c_size_t
 
 _SIGNATURES = {
     "w4_pack": (_I32, [_P, _I32, _I32, _I32, _P, _P, _P]),
+    "w4_tile": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
     "fp8_quant_static": (_I32, [_P, _I64, _F32, _P, _P]),
     "moe_route_sort": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "moe_gemm1_w4a8": (_I32, [_P, _I32, _F32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
@@ -130,15 +131,32 @@ def _workspace(nbytes, device):
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def w4_pack(w):
-    """bf16 [E, N, K] -> (packed int32 [E, N, K/8], scale fp32 [E, N])."""
+def w4_pack(w, tiled=False):
+    """bf16 [E, N, K] -> (packed int32 [E, N, K/8], scale fp32 [E, N]); with tiled=True the
+    words come in the layout the MoE GEMMs read, int32 [E, N/16, K/128, 256] (w4_tile)."""
     torch = _torch()
     E, N, K = w.shape
     _need(w, torch.bfloat16, (E, N, K), "w")
     packed = torch.empty((E, N, K // 8), dtype=torch.int32, device=w.device)
     scale = torch.empty((E, N), dtype=torch.float32, device=w.device)
     _check("w4_pack", lib().w4_pack(_ptr(w), E, N, K, _ptr(packed), _ptr(scale), _stream(w.device)))
+    if tiled:
+        packed = w4_tile(packed)
     return packed, scale
+
+
+def w4_tile(packed, out=None):
+    """packed int32 [E, N, K/8] (w4_pack) -> the tiled layout int32 [E, N/16, K/128, 256]."""
+    torch = _torch()
+    E, N, K8 = packed.shape
+    K = K8 * 8
+    _need(packed, torch.int32, (E, N, K8), "packed")
+    shape = (E, N // 16, K // 128, 256)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.int32, device=packed.device)
+    _need(out, torch.int32, shape, "tiled")
+    _check("w4_tile", lib().w4_tile(_ptr(packed), E, N, K, _ptr(out), _stream(packed.device)))
+    return out
 
 
 def fp8_quant_static(x, s, out=None):
@@ -185,11 +203,13 @@ def moe_gemm1_w4a8(x, s_x, w13, s_w13, offsets, sorted_pair, act, s_a, debug=Fal
     """x bf16 [T, H] or uint8 E4M3 codes [T, H]; returns a_fp8 uint8 [2T, I] (and fp32 [2T, 2I] if debug)."""
     torch = _torch()
     T, H = x.shape
-    E, N2, H8 = w13.shape
-    I = N2 // 2
+    if w13.dim() != 4:
+        raise ValueError("w13: expected the tiled layout [E, 2I/16, H/128, 256] (w4_tile)")
+    E, NB, KT, _ = w13.shape
+    I = NB * 8
     dt = DT_BF16 if x.dtype == torch.bfloat16 else DT_E4M3
     _need(x, torch.bfloat16 if dt == DT_BF16 else torch.uint8, (T, H), "x")
-    _need(w13, torch.int32, (E, 2 * I, H // 8), "w13")
+    _need(w13, torch.int32, (E, 2 * I // 16, H // 128, 256), "w13 (tiled)")
     _need(s_w13, torch.float32, (E, 2 * I), "s_w13")
     _need(offsets, torch.int32, (E + 1,), "offsets")
     _need(sorted_pair, torch.int32, (2 * T,), "sorted_pair")
@@ -211,9 +231,12 @@ def moe_gemm2_w4a8(a, s_a, w2, s_w2, offsets, pair_pos, topk_w, out_dtype="bf16"
     torch = _torch()
     P, I = a.shape
     T = P // 2
-    E, H, I8 = w2.shape
+    if w2.dim() != 4:
+        raise ValueError("w2: expected the tiled layout [E, H/16, I/128, 256] (w4_tile)")
+    E, HB, _, _ = w2.shape
+    H = HB * 16
     _need(a, torch.uint8, (2 * T, I), "a_fp8")
-    _need(w2, torch.int32, (E, H, I // 8), "w2")
+    _need(w2, torch.int32, (E, H // 16, I // 128, 256), "w2 (tiled)")
     _need(s_w2, torch.float32, (E, H), "s_w2")
     _need(offsets, torch.int32, (E + 1,), "offsets")
     _need(pair_pos, torch.int32, (2 * T,), "pair_pos")
@@ -257,7 +280,8 @@ def fp8_block_linear(x, w, s, out=None):
 
 
 def moe_layer(x, s_x, logits, w13, s_w13, w2, s_w2, act, s_a, out_dtype="bf16"):
-    """The whole layer: route+sort, gate|up, down+combine (x bf16 or E4M3 codes)."""
+    """The whole layer: route+sort, gate|up, down+combine (x bf16 or E4M3 codes; w13 and w2
+    in the tiled layout)."""
     r = moe_route_sort(logits)
     a = moe_gemm1_w4a8(x, s_x, w13, s_w13, r["offsets"], r["sorted_pair"], act, s_a)
     return moe_gemm2_w4a8(a, s_a, w2, s_w2, r["offsets"], r["pair_pos"], r["weights"], out_dtype)

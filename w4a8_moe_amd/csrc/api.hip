@@ -101,6 +101,18 @@ int32_t w4_pack(const uint16_t* w_bf16, int32_t E, int32_t N, int32_t K, int32_t
   return launch_status();
 }
 
+int32_t w4_tile(const int32_t* packed, int32_t E, int32_t N, int32_t K, int32_t* tiled, void* stream) {
+  if (!packed || !tiled) return W4A8_ERR_NULL;
+  if (E < 1 || N < kTileRows || K < kTileK || N % kTileRows != 0 || K % kTileK != 0) return W4A8_ERR_SHAPE;
+  if ((int64_t)E * N >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;
+  if (!aligned16(packed) || !aligned16(tiled)) return W4A8_ERR_ALIGN;
+  const uint64_t bytes = (uint64_t)E * N * (uint64_t)(K / 2);
+  const uint64_t a = reinterpret_cast<uint64_t>(packed), b = reinterpret_cast<uint64_t>(tiled);
+  if (a < b + bytes && b < a + bytes) return W4A8_ERR_ARG;         // the two must not overlap
+  launch_w4_tile(packed, E, N, K, tiled, as_stream(stream));
+  return launch_status();
+}
+
 int32_t fp8_quant_static(const uint16_t* x_bf16, int64_t n, float s, uint8_t* out, void* stream) {
   if (n < 0) return W4A8_ERR_SHAPE;
   if (!good_scale(s)) return W4A8_ERR_ARG;

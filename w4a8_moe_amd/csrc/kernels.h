@@ -6,9 +6,17 @@
 #include <stdint.h>
 
 namespace w4a8 {
+// Tiled int4 weight layout read by the MoE GEMMs: per expert, [N/16][K/128] tiles of
+// 1 KB, k-steps of one 16-row block consecutive; in tile (nb, ks) the 16 bytes at
+// 16 * (i + 16 g) are bytes 64 ks + 16 g .. +16 of row 16 nb + i of the packed matrix.
+// One 16-byte load per lane fetches a whole tile, and lane (i, g) then holds
+// K = 128 ks + 32 g .. +32 of row i, the order the matrix instructions take.
+constexpr int kTileRows = 16, kTileK = 128;
+constexpr uint32_t kTileBytes = 1024;
 
 // ---- quant.hip
 void launch_w4_pack(const uint16_t* w, int64_t rows, int K, int32_t* packed, float* scale, hipStream_t st);
+void launch_w4_tile(const int32_t* packed, int64_t E, int N, int K, int32_t* tiled, hipStream_t st);
 void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st);
 void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st);
 

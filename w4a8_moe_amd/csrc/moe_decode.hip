@@ -17,22 +17,24 @@
 // (16x16x32) and accumulates exactly as the method states. The tiled prefill kernel,
 // bound by the matrix cores, uses the fp8 MFMA.
 //
-// int4 -> fp16 in registers, 1 VALU op per weight: XOR with 0x8 turns a nibble q into
-// q + 8 in [0, 15]; the E4M3 code c in [0, 15] has the value c * 2^-9 (subnormals then
-// the first binade), so masking the nibbles into bytes gives exact E4M3 codes of
-// (q + 8) * 2^-9, and v_cvt_scalef32_pk_f16_fp8 widens two of them per op to normal
-// fp16 values. A third MFMA per 32-K step multiplies the same activations by the
-// constant -8 * 2^-9 and removes the offset; the sums are exact in fp32 before that
-// subtraction, so only fp32 rounding is left.
+// int4 -> fp16 in registers, 10 VALU ops per 8 weights, exact: flipping the top bit of a
+// nibble turns q into c = q + 8 in [0, 15]; a byte permute places the low nibbles' c under
+// the fp16 exponent of 1024 (bits 0x6400 | c = 1024 + c, two values per op) and one packed
+// fp16 subtraction of 1032 leaves q. The high nibbles stay where they are (1024 + 16 c,
+// minus 1152: 16 q), and the activations they meet are staged divided by 16, so no shift
+// is needed. (Codes placed as fp16 subnormals would need no subtraction, but the fp16
+// MFMA loses precision on subnormal operands: measured on MI355X, a K = 14336 down
+// projection erred by 5e-6 of its largest output instead of 1e-8.)
 //
 // Mapping. A workgroup = 8 waves on one expert and one K-slice. The activation rows of
-// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS as E4M3
-// codes, in the order the MFMA B operand is read (one ds_read_b64 per lane, 512 bytes
-// per wave without bank conflicts), and widened to fp16 as they are read. Each wave owns
-// two blocks of 16 weight rows (gate rows n..n+15 and up rows I+n..I+n+15, or two blocks
-// of down rows) and streams them with 16-byte buffer loads, kDepth k-steps (of 128)
-// ahead, without a break at LDS chunk boundaries; one load instruction of a wave covers
-// 64 contiguous bytes of 16 rows.
+// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS widened
+// to fp16, in the order the MFMA B operand is read (one ds_read_b128 per lane and
+// instruction, 1 KB per wave without bank conflicts). Each wave owns two blocks of 16
+// weight rows (gate rows n..n+15 and up rows I+n..I+n+15, or two blocks of down rows) and
+// streams them with 16-byte buffer loads, kDepth k-steps (of 128) ahead, without a break
+// at LDS chunk boundaries. The weights are in the tiled layout (w4_tile): one load
+// instruction of a wave fetches one contiguous 1 KB tile (16 rows x 128 K), and a wave's
+// whole stream over K is contiguous.
 #include <algorithm>
 
 #include "common.h"
@@ -55,7 +57,7 @@ namespace w4a8 {
 #endif
 constexpr int kDepth = W4A8_DECODE_DEPTH;
 constexpr int kBody = W4A8_DECODE_BODY;                    // k-steps per unrolled loop body
-constexpr int kStageBatch = 8;                             // staging units in flight per thread
+constexpr int kStageBatch = 4;                             // staging units in flight per thread
 static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
 constexpr int kWeightLoadAux = W4A8_DECODE_NT_LOADS ? 2 : 0;   // cache-policy bits: nt
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
@@ -64,17 +66,34 @@ __device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_ca
 
 // two E4M3 codes (bytes 0,1 or, with HIGH, bytes 2,3) -> two fp16 values, exact
 template <bool HIGH>
-__device__ __forceinline__ uint32_t cvt2_e4m3_f16(uint32_t codes) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, 1.0f, HIGH));
+__device__ __forceinline__ uint32_t cvt2_e4m3_f16(uint32_t codes, float scale = 1.0f) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, scale, HIGH));
 }
 
-// One packed word (8 int4 codes, reorder layout) -> 8 fp16 values (q + 8) * 2^-9 in K order.
-__device__ __forceinline__ v8h int4x8_to_f16_offset(uint32_t w) {
-  const uint32_t lo = (w & 0x0F0F0F0Fu) ^ 0x08080808u;          // codes of elements 0..3
-  const uint32_t hi = ((w >> 4) & 0x0F0F0F0Fu) ^ 0x08080808u;   // codes of elements 4..7
-  v4i r = {(int)cvt2_e4m3_f16<false>(lo), (int)cvt2_e4m3_f16<true>(lo),
-           (int)cvt2_e4m3_f16<false>(hi), (int)cvt2_e4m3_f16<true>(hi)};
-  return __builtin_bit_cast(v8h, r);
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+
+// bytes 0,1 (SEL 0x04010400) or 2,3 (SEL 0x04030402) of x placed under the fp16 exponent
+// of 1024: the pair 1024 + x_byte (exact for any byte)
+template <uint32_t SEL>
+__device__ __forceinline__ v2h f16_1024_plus(uint32_t x) {
+  return __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x, SEL));
+}
+
+// One packed word (8 int4 codes, reorder layout) -> 8 exact fp16 values in K order:
+// q for elements 0..3 and 16 q for elements 4..7 (whose activations are staged / 16).
+// c = q + 8 is the nibble with its top bit flipped; the low nibbles give 1024 + c, the
+// high nibbles, left in place, 1024 + 16 c.
+__device__ __forceinline__ v8h int4x8_to_f16(uint32_t w, uint32_t mlo, uint32_t mhi) {
+  const uint32_t lo = (w ^ 0x88888888u) & mlo;                   // c of elements 0..3
+  const uint32_t hi = (w ^ 0x88888888u) & mhi;                   // 16 c of elements 4..7
+  const v2h off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};     // 1024 + 8
+  const v2h off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};     // 1024 + 16 * 8
+  const v2h e01 = f16_1024_plus<0x04010400u>(lo) - off_lo, e23 = f16_1024_plus<0x04030402u>(lo) - off_lo;
+  const v2h e45 = f16_1024_plus<0x04010400u>(hi) - off_hi, e67 = f16_1024_plus<0x04030402u>(hi) - off_hi;
+  v8h r;
+  r[0] = e01[0]; r[1] = e01[1]; r[2] = e23[0]; r[3] = e23[1];
+  r[4] = e45[0]; r[5] = e45[1]; r[6] = e67[0]; r[7] = e67[1];
+  return r;
 }
 
 __device__ __forceinline__ v4f mfma_f16(v8h a, v8h b, v4f c) {
@@ -95,23 +114,22 @@ __device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off
 }
 
 
-// One k-step (128 K) of one wave: 4 MFMAs of K = 32 per weight block and column tile,
-// plus the offset correction, B read from the fp16 LDS chunk.
-template <int MAXT>
+// One k-step (128 K) of one wave: 4 MFMAs of K = 32 per weight block and column tile
+// (the first nt of NT tiles), B read from the fp16 LDS chunk.
+template <int NT>
 __device__ __forceinline__ void mma_step(const uint4& a0, const uint4& a1, const uint8_t* lds, int s, int S, int nt,
-                                         int lane, const v8h& corr_op, v4f* acc0, v4f* acc1, v4f* corr) {
+                                         int lane, uint32_t mlo, uint32_t mhi, v4f* acc0, v4f* acc1) {
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
-    const v8h A0 = int4x8_to_f16_offset(word_of(a0, m));
-    const v8h A1 = int4x8_to_f16_offset(word_of(a1, m));
+    const v8h A0 = int4x8_to_f16(word_of(a0, m), mlo, mhi);
+    const v8h A1 = int4x8_to_f16(word_of(a1, m), mlo, mhi);
 #pragma unroll
-    for (int j = 0; j < MAXT; ++j) {
+    for (int j = 0; j < NT; ++j) {
       if (j < nt) {
         const v8h b = __builtin_bit_cast(
             v8h, *reinterpret_cast<const uint4*>(lds + ((j * S + s) * 4 + m) * 1024 + lane * 16));
         acc0[j] = mfma_f16(A0, b, acc0[j]);
         acc1[j] = mfma_f16(A1, b, acc1[j]);
-        corr[j] = mfma_f16(corr_op, b, corr[j]);
       }
     }
   }
@@ -119,16 +137,46 @@ __device__ __forceinline__ void mma_step(const uint4& a0, const uint4& a1, const
 
 // Consume one k-step from the register ring, then refill the same registers with the
 // k-step kDepth ahead (out-of-range offsets past this wave's K-range move no data).
-template <int MAXT>
+template <int NT>
 __device__ __forceinline__ void stream_step(uint4& q0, uint4& q1, __amdgpu_buffer_rsrc_t wr, uint32_t off0,
                                             uint32_t off1, int ST, int ST1, int gstep, const uint8_t* lds, int s,
-                                            int S, int nt, int lane, const v8h& corr_op, v4f* acc0, v4f* acc1,
-                                            v4f* corr) {
-  mma_step<MAXT>(q0, q1, lds, s, S, nt, lane, corr_op, acc0, acc1, corr);
+                                            int S, int nt, int lane, uint32_t mlo, uint32_t mhi, v4f* acc0,
+                                            v4f* acc1) {
+  mma_step<NT>(q0, q1, lds, s, S, nt, lane, mlo, mhi, acc0, acc1);
   __builtin_amdgcn_sched_barrier(0);                        // keep the refill after the use
   const int nxt = gstep + kDepth;
-  q0 = buf_ld16(wr, nxt < ST ? off0 + nxt * 64 : kOutOfRange);
-  q1 = buf_ld16(wr, nxt < ST1 ? off1 + nxt * 64 : kOutOfRange);
+  q0 = buf_ld16(wr, nxt < ST ? off0 + nxt * kTileBytes : kOutOfRange);
+  q1 = buf_ld16(wr, nxt < ST1 ? off1 + nxt * kTileBytes : kOutOfRange);
+}
+
+// The S k-steps of one LDS chunk against the column tiles (see mma_step). Full rounds of
+// kDepth k-steps issue a load for every step they consume (no branch around any load);
+// only the last chunk can end with a partial round, which issues no loads. The compiler
+// drains all outstanding loads at every loop header, so the k-steps run in unrolled
+// bodies of kBody steps (precise waits inside), then in rounds of kDepth.
+template <int NT>
+__device__ __forceinline__ void stream_chunk(uint4 (&q0)[kDepth], uint4 (&q1)[kDepth], __amdgpu_buffer_rsrc_t wr,
+                                             uint32_t off0, uint32_t off1, int ST, int ST1, int sg,
+                                             const uint8_t* lds, int S, int nt, int lane, uint32_t mlo,
+                                             uint32_t mhi, v4f* acc0, v4f* acc1) {
+  constexpr int body = NT <= 2 ? kBody : kDepth;            // keep 4-tile code within registers
+  int s = 0;
+  for (; s + body <= S; s += body) {
+#pragma unroll
+    for (int t = 0; t < body; ++t)
+      stream_step<NT>(q0[t % kDepth], q1[t % kDepth], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt, lane,
+                      mlo, mhi, acc0, acc1);
+  }
+  for (; s + kDepth <= S; s += kDepth) {
+#pragma unroll
+    for (int t = 0; t < kDepth; ++t)
+      stream_step<NT>(q0[t], q1[t], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt, lane, mlo, mhi, acc0,
+                      acc1);
+  }
+  const int rem = S - s;
+#pragma unroll
+  for (int d = 0; d < kDepth - 1; ++d)
+    if (d < rem) mma_step<NT>(q0[d], q1[d], lds, s + d, S, nt, lane, mlo, mhi, acc0, acc1);
 }
 
 template <bool GATEUP, int MAXT>
@@ -143,7 +191,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const int seg0 = p.offsets[e];
   const int cnt = p.offsets[e + 1] - seg0;
   if (cnt <= 0) return;                                     // untouched expert: no weight traffic
-  const int nt = min((cnt + 15) >> 4, MAXT);
+  const int nt = min((cnt + 15) >> 4, MAXT);                // column tiles holding rows
   const int k_begin = slice * p.kslice;
   const int k_end = min(p.K, k_begin + p.kslice);
   const int kc_max = ((p.lds_bytes / (32 * nt)) / (128 * kDepth)) * (128 * kDepth);   // fp16 rows of 16*nt tokens
@@ -159,26 +207,27 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const uint8_t*>(p.w) + (size_t)e * p.Nw * row_bytes), (short)0,
       (int)(p.Nw * row_bytes), 0x00020000);
-  const uint32_t off0 = (uint32_t)(blk0 * 16 + i) * row_bytes + g * 16 + k_begin / 2;
-  const uint32_t off1 = (uint32_t)((has1 ? blk1 : blk0) * 16 + i) * row_bytes + g * 16 + k_begin / 2;
+  // tiled weights: the 1 KB tile (16 rows x 128 K) of a block and k-step, in lane order
+  const uint32_t off0 = (uint32_t)(blk0 * 16) * row_bytes + (k_begin / 128) * kTileBytes + lane * 16;
+  const uint32_t off1 = (uint32_t)((has1 ? blk1 : blk0) * 16) * row_bytes + (k_begin / 128) * kTileBytes + lane * 16;
   const int ST = has_work ? (k_end - k_begin) >> 7 : 0;    // k-steps of 128 this wave streams
   const int ST1 = has1 ? ST : 0;
 
-  v4f acc0[MAXT], acc1[MAXT], corr[MAXT];
+  v4f acc0[MAXT], acc1[MAXT];
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
-    acc0[j] = v4f{0.f, 0.f, 0.f, 0.f}; acc1[j] = acc0[j]; corr[j] = acc0[j];
+    acc0[j] = v4f{0.f, 0.f, 0.f, 0.f}; acc1[j] = acc0[j];
   }
-  v8h corr_op;
-#pragma unroll
-  for (int r = 0; r < 8; ++r) corr_op[r] = (_Float16)(-8.0f / 512.0f);
+  // nibble masks held in registers (one v_bitop3 per mask and word)
+  uint32_t mlo = 0x0F0F0F0Fu, mhi = 0xF0F0F0F0u;
+  asm volatile("" : "+v"(mlo), "+v"(mhi));
 
   // prefetch the first kDepth k-steps; the stream runs on across chunk boundaries
   uint4 q0[kDepth], q1[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    q0[d] = buf_ld16(wr, d < ST ? off0 + d * 64 : kOutOfRange);
-    q1[d] = buf_ld16(wr, d < ST1 ? off1 + d * 64 : kOutOfRange);
+    q0[d] = buf_ld16(wr, d < ST ? off0 + d * kTileBytes : kOutOfRange);
+    q1[d] = buf_ld16(wr, d < ST1 ? off1 + d * kTileBytes : kOutOfRange);
   }
   int sg = 0;                                               // k-steps consumed so far
   for (int kc0 = k_begin; kc0 < k_end; kc0 += kc_max) {
@@ -216,37 +265,17 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
         for (int b = 0; b < kStageBatch; ++b) {
           const int v = v0 + b * kDecodeWaves * kWave + tid;
           if (v >= slots) break;
+          // codes 4..7 of each 8 face the weights' high nibbles (16 q): staged divided by 16
           const uint4 w = make_uint4(cvt2_e4m3_f16<false>(q[b].x), cvt2_e4m3_f16<true>(q[b].x),
-                                     cvt2_e4m3_f16<false>(q[b].y), cvt2_e4m3_f16<true>(q[b].y));
+                                     cvt2_e4m3_f16<false>(q[b].y, 0.0625f), cvt2_e4m3_f16<true>(q[b].y, 0.0625f));
           *reinterpret_cast<uint4*>(lds + (size_t)v * 16) = w;
         }
       }
     }
     lds_barrier();
-    // ---- stream the weights of this chunk: full rounds of kDepth k-steps issue a load
-    //      for every step they consume (no branch around any load); only the last chunk
-    //      can end with a partial round, which issues no loads
+    // ---- stream the weights of this chunk
     if (has_work) {
-      // The compiler drains all outstanding loads at every loop header, so the k-steps run
-      // in unrolled bodies of kBody steps (precise waits inside), then in rounds of kDepth.
-      constexpr int body = MAXT <= 2 ? kBody : kDepth;     // keep 4-tile code within registers
-      int s = 0;
-      for (; s + body <= S; s += body) {
-#pragma unroll
-        for (int t = 0; t < body; ++t)
-          stream_step<MAXT>(q0[t % kDepth], q1[t % kDepth], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt,
-                            lane, corr_op, acc0, acc1, corr);
-      }
-      for (; s + kDepth <= S; s += kDepth) {
-#pragma unroll
-        for (int t = 0; t < kDepth; ++t)
-          stream_step<MAXT>(q0[t], q1[t], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt, lane, corr_op,
-                            acc0, acc1, corr);
-      }
-      const int rem = S - s;                                // last chunk only; issues no loads
-#pragma unroll
-      for (int d = 0; d < kDepth - 1; ++d)
-        if (d < rem) mma_step<MAXT>(q0[d], q1[d], lds, s + d, S, nt, lane, corr_op, acc0, acc1, corr);
+      stream_chunk<MAXT>(q0, q1, wr, off0, off1, ST, ST1, sg, lds, S, nt, lane, mlo, mhi, acc0, acc1);
     }
     sg += S;
   }
@@ -254,7 +283,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
 
   // ---- epilogue: lane holds rows 4g..4g+3 of each block, column (token row) j*16 + i
   const float* ws = p.w_scale + (size_t)e * p.Nw;
-  const float k0 = 512.0f * p.s_act;                        // undo the 2^-9 of the offset codes
+  const float k0 = p.s_act;
 #pragma unroll
   for (int j = 0; j < MAXT; ++j) {
     const int col = j * 16 + i;
@@ -268,8 +297,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
       const float sgv[4] = {sg4.x, sg4.y, sg4.z, sg4.w}, suv[4] = {su4.x, su4.y, su4.z, su4.w};
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        gv[v] = (acc0[j][v] + corr[j][v]) * k0 * sgv[v];
-        uv[v] = (acc1[j][v] + corr[j][v]) * k0 * suv[v];
+        gv[v] = acc0[j][v] * k0 * sgv[v];
+        uv[v] = acc1[j][v] * k0 * suv[v];
         av[v] = div_rn(act_fast_rt(gv[v], p.act_fn) * uv[v], p.s_a, p.inv_s_a);
       }
       *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
@@ -286,10 +315,10 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
         const v4f acc = b == 0 ? acc0[j] : acc1[j];
         const float4 sw = *reinterpret_cast<const float4*>(ws + nb);
         float4 o;
-        o.x = (acc[0] + corr[j][0]) * k0 * sw.x;
-        o.y = (acc[1] + corr[j][1]) * k0 * sw.y;
-        o.z = (acc[2] + corr[j][2]) * k0 * sw.z;
-        o.w = (acc[3] + corr[j][3]) * k0 * sw.w;
+        o.x = acc[0] * k0 * sw.x;
+        o.y = acc[1] * k0 * sw.y;
+        o.z = acc[2] * k0 * sw.z;
+        o.w = acc[3] * k0 * sw.w;
         *reinterpret_cast<float4*>(p.partial + ((size_t)slice * p.P + r) * p.n_out + nb) = o;
       }
     }

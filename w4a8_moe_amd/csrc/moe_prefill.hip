@@ -146,7 +146,8 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   // first channel of the tile: gate|up -> 128 channels (gate rows + the matching up rows)
   const int n0 = GATEUP ? ntile * (kPN / 2) : ntile * kPN;
 
-  // ---- this lane's weight rows: block a of the wave, row i of the block, K-part g
+  // ---- this lane's weights: block a of the wave, the 16 bytes at lane * 16 of each of the
+  //      block's tiles (row i, K-part g of a 16-row x 128-K tile)
   const uint32_t row_bytes = (uint32_t)p.K / 2;
   const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(reinterpret_cast<const uint8_t*>(p.w) + (size_t)o.e * p.Nw * row_bytes), (short)0,
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     // gate|up: blocks 0,1 gate channels n0 + 32 w + 16 (a % 2) + i, blocks 2,3 their up rows
     const int chan = GATEUP ? n0 + 32 * wave + 16 * (a & 1) + i : n0 + 64 * wave + 16 * a + i;
     const int grow = GATEUP && a >= 2 ? chan + p.n_out : chan;
-    woff[a] = chan < (GATEUP ? p.n_out : p.Nw) ? (uint32_t)grow * row_bytes + 16 * g : kPOutOfRange;
+    woff[a] = chan < (GATEUP ? p.n_out : p.Nw) ? (uint32_t)(grow - i) * row_bytes + 16 * lane : kPOutOfRange;
   }
 
   // ---- token staging: chunk c = tid + 256 j is tile row c / 8, 16-byte part c % 8.
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   uint4 w0[4], w1[4];          // raw weights of steps s and s+1
   auto load_weights = [&](uint4 (&w)[4], int s) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) w[a] = pf_ld16(wr, woff[a] + (uint32_t)(s * 64));
+    for (int a = 0; a < 4; ++a) w[a] = pf_ld16(wr, woff[a] + (uint32_t)(s * kTileBytes));
   };
 
   // ---- prologue: weights of steps 0..2 in flight, tokens of step 0 in LDS, of step 1 in flight
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
       }
       // words wi are converted at bb = wi (16 blocks): block a's last word goes at bb = 4 a + 3
       static_assert(kTB == 16, "the reload points below follow the conversion order for 16 blocks");
-      if ((bb & 3) == 3) w1[bb >> 2] = pf_ld16(wr, woff[bb >> 2] + (uint32_t)((s + 2) * 64));
+      if ((bb & 3) == 3) w1[bb >> 2] = pf_ld16(wr, woff[bb >> 2] + (uint32_t)((s + 2) * kTileBytes));
       __builtin_amdgcn_sched_barrier(0);
       if (bb < kTB - 1) bcur = bnext;
     }

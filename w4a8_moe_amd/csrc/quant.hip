@@ -10,6 +10,8 @@
 //    "qwen4_exp: serve the block-FP8 dense projections natively (+25% decode)").
 // All quotients are formed with the correctly rounded fp32 division (the library is
 // built without fast-math), then rounded to nearest even.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -68,6 +70,28 @@ __global__ __launch_bounds__(kPackThreads) void w4_pack_kernel(
 void launch_w4_pack(const uint16_t* w, int64_t rows, int K, int32_t* packed, float* scale, hipStream_t st) {
   // rows <= E * N < 2^31 is checked by the caller
   hipLaunchKernelGGL(w4_pack_kernel, dim3((unsigned)rows), dim3(kPackThreads), 0, st, w, K, packed, scale);
+}
+
+// -------------------------------------------------------------------- w4_tile
+// One thread per 16 output bytes: writes are contiguous, each read is 16 bytes of a row.
+__global__ __launch_bounds__(256) void w4_tile_kernel(const uint4* __restrict__ src, int64_t units, int N, int K,
+                                                      uint4* __restrict__ dst) {
+  const int64_t kt = K / kTileK, nb_per_e = N / kTileRows, row_units = K / 32;   // 16-byte units of a row
+  for (int64_t u = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; u < units; u += (int64_t)gridDim.x * blockDim.x) {
+    const int lane = (int)(u & 63);
+    const int64_t tile = u >> 6;
+    const int64_t ks = tile % kt, blk = tile / kt;               // blk = e * N/16 + nb
+    const int64_t e = blk / nb_per_e, nb = blk - e * nb_per_e;
+    const int64_t row = e * N + nb * kTileRows + (lane & 15);
+    dst[u] = src[row * row_units + ks * 4 + (lane >> 4)];
+  }
+}
+
+void launch_w4_tile(const int32_t* packed, int64_t E, int N, int K, int32_t* tiled, hipStream_t st) {
+  const int64_t units = E * N * (int64_t)(K / 32);
+  const unsigned grid = (unsigned)std::min<int64_t>((units + 255) / 256, 65536);
+  hipLaunchKernelGGL(w4_tile_kernel, dim3(grid), dim3(256), 0, st, reinterpret_cast<const uint4*>(packed), units, N,
+                     K, reinterpret_cast<uint4*>(tiled));
 }
 
 // -------------------------------------------------------------------- fp8_quant_static
