@@ -276,7 +276,8 @@ def test_fp8_block_quant_bit_exact(N, K):
     assert same_codes(host(q), rq).all()
 
 
-@pytest.mark.parametrize("M,N,K", [(1, 256, 384), (8, 400, 256), (16, 128, 2048), (3, 1024, 2560), (12, 64, 2560)])
+@pytest.mark.parametrize("M,N,K", [(1, 256, 384), (8, 400, 256), (16, 128, 2048), (3, 1024, 2560), (12, 64, 2560),
+                                   (2, 48, 384), (5, 80, 1152), (1, 16, 128)])
 def test_fp8_block_linear_parity(M, N, K):
     cfg = synth.custom_block("bl", M=M, N=N, K=K, cfg=400 + M)
     w = synth.block_weights(cfg)

@@ -10,16 +10,32 @@
 // multiplied against the bf16 activations with fp32 accumulation. Each 128-column block
 // is accumulated on its own and added to the running sum with its scale.
 //
-// Mapping: a workgroup of 4 waves covers 64 output rows, one 16-row block per wave, all
-// of K. The M <= 16 activation rows are staged once per workgroup in LDS, compactly
-// (no padding columns). Weight loads are 2 x 16 B per lane per 128-K block.
+// Mapping: a 16-row block is owned by kBlSplit (4) waves, each streaming one contiguous
+// quarter of K; their partial sums meet in LDS and are added in wave order
+// (deterministic). A workgroup holds RB such row blocks (2 for M <= 2, 4 above: the M
+// activation rows are staged once per workgroup in LDS, compactly, so a larger M wants
+// more rows to share them). A GEMV has no other parallelism to hide HBM latency with:
+// splitting K gives 4 N/16 waves. Weight loads are 2 x 16 B per lane per 128-K block,
+// kBlDepth blocks ahead (one: the many waves in flight hide the latency; measured best).
+//
+// Tuning knobs (defaults chosen by measurement on MI355X): W4A8_BL_SPLIT waves per row
+// block, W4A8_BL_DEPTH blocks in flight, W4A8_BL_RB_SMALL_M / W4A8_BL_RB_LARGE_M row
+// blocks per workgroup for M <= 2 / M > 2.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
 namespace w4a8 {
 
-constexpr int kBlWaves = 4;
-constexpr int kBlDepth = 4;     // 128-K blocks of weights in flight per wave
+#ifndef W4A8_BL_SPLIT
+#define W4A8_BL_SPLIT 4
+#endif
+constexpr int kBlSplit = W4A8_BL_SPLIT;   // waves per 16-row block, each on a part of K
+#ifndef W4A8_BL_DEPTH
+#define W4A8_BL_DEPTH 1
+#endif
+constexpr int kBlDepth = W4A8_BL_DEPTH;   // 128-K blocks of weights in flight per wave
 
 // 4 E4M3 codes -> 4 bf16 values in two dwords (exact).
 __device__ __forceinline__ void e4m3x4_to_bf16x4(uint32_t c, uint32_t& lo, uint32_t& hi) {
@@ -35,16 +51,18 @@ __device__ __forceinline__ v8bf bf16_operand(uint32_t d0, uint32_t d1, uint32_t 
   return __builtin_bit_cast(v8bf, t);
 }
 
-__global__ __launch_bounds__(kBlWaves * kWave) void fp8_block_linear_kernel(
+template <int RB>   // 16-row blocks per workgroup
+__global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, const float* __restrict__ S,
     int M, int N, int K, uint16_t* __restrict__ y) {
+  constexpr int kWaves = RB * kBlSplit;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int KB = K >> 7;
   // ---- stage x: unit (kb, j, g, m) = 8 bf16 = x[m][kb*128 + g*32 + j*8 .. +8], stored at
   //      ((kb*4 + j)*4 + g)*M + m, so lane (m, g) of MFMA j reads 16 contiguous bytes.
   const int units = M * (K >> 3);
-  for (int u = tid; u < units; u += kBlWaves * kWave) {
+  for (int u = tid; u < units; u += kWaves * kWave) {
     const int m = u / (K >> 3), c8 = u - m * (K >> 3);       // 8-element chunk of row m
     const int kb = c8 >> 4, within = c8 & 15;                // 16 chunks per 128-K block
     const int g = within >> 2, j = within & 3;
@@ -52,25 +70,32 @@ __global__ __launch_bounds__(kBlWaves * kWave) void fp8_block_linear_kernel(
     *reinterpret_cast<uint4*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 4)) = v;
   }
   __syncthreads();
-  const int rb = blockIdx.x * kBlWaves + wave;               // 16-row block
-  if (rb * 16 >= N) return;
+  const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);   // 16-row block
+  const bool rb_ok = blockIdx.x * RB + wave / kBlSplit < N / 16;      // else: no K blocks, no store
+  const int part_k = wave % kBlSplit;
   const int i = lane & 15, g = lane >> 4;
   const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
   const float* srow = S + (size_t)((rb * 16) >> 7) * KB;
   const bool col_ok = i < M;
+  // this wave's 128-K blocks [kb_begin, kb_end)
+  const int per = (KB + kBlSplit - 1) / kBlSplit;
+  const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
 
   v4f acc = {0.f, 0.f, 0.f, 0.f};
   uint4 q0[kBlDepth], q1[kBlDepth];
 #pragma unroll
   for (int d = 0; d < kBlDepth; ++d)
-    if (d < KB) { q0[d] = *reinterpret_cast<const uint4*>(wp + d * 128); q1[d] = *reinterpret_cast<const uint4*>(wp + d * 128 + 16); }
-  for (int kb0 = 0; kb0 < KB; kb0 += kBlDepth) {
+    if (kb_begin + d < kb_end) {
+      q0[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128);
+      q1[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128 + 16);
+    }
+  for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kBlDepth) {
 #pragma unroll
     for (int d = 0; d < kBlDepth; ++d) {
       const int kb = kb0 + d;
-      if (kb < KB) {
+      if (kb < kb_end) {
         const uint4 a0 = q0[d], a1 = q1[d];
-        if (kb + kBlDepth < KB) {
+        if (kb + kBlDepth < kb_end) {
           q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128);
           q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128 + 16);
         }
@@ -92,8 +117,19 @@ __global__ __launch_bounds__(kBlWaves * kWave) void fp8_block_linear_kernel(
       }
     }
   }
+  // ---- the partial sums of a row block's waves meet in LDS over the staged x (once every
+  //      wave is done with it): its K-part 0 wave adds parts 1, 2, 3 in order
+  v4f* part = reinterpret_cast<v4f*>(lds);
+  __syncthreads();
+  if (part_k > 0) part[(wave - 1) * kWave + lane] = acc;     // slot of wave w: w - 1
+  __syncthreads();
+  if (part_k > 0 || !col_ok || !rb_ok) return;
+#pragma unroll
+  for (int v = 1; v < kBlSplit; ++v) {
+    const v4f o = part[(wave + v - 1) * kWave + lane];
+    acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+  }
   // lane holds rows rb*16 + 4g + v of column (token) i
-  if (!col_ok) return;
   const int n = rb * 16 + 4 * g;
   uint2 o;
   o.x = f32_to_bf16_bits(acc[0]) | f32_to_bf16_bits(acc[1]) << 16;
@@ -101,12 +137,28 @@ __global__ __launch_bounds__(kBlWaves * kWave) void fp8_block_linear_kernel(
   *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
 }
 
+template <int RB>
+static void launch_bl(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K, uint16_t* y,
+                      hipStream_t st) {
+  const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);   // N % 16 == 0 is checked by the caller
+  // staged x, later reused for the partial sums
+  const size_t lds =
+      std::max((size_t)M * K * sizeof(uint16_t), (size_t)(RB * kBlSplit - 1) * kWave * sizeof(v4f));
+  hipLaunchKernelGGL(fp8_block_linear_kernel<RB>, dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, x, w, s, M, N,
+                     K, y);
+}
+
 void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K,
                              uint16_t* y, hipStream_t st) {
-  const int rows_per_wg = kBlWaves * 16;
-  const unsigned grid = (unsigned)((N + rows_per_wg - 1) / rows_per_wg);
-  const size_t lds = (size_t)M * K * sizeof(uint16_t);
-  hipLaunchKernelGGL(fp8_block_linear_kernel, dim3(grid), dim3(kBlWaves * kWave), lds, st, x, w, s, M, N, K, y);
+#ifndef W4A8_BL_RB_SMALL_M
+#define W4A8_BL_RB_SMALL_M 2
+#endif
+#ifndef W4A8_BL_RB_LARGE_M
+#define W4A8_BL_RB_LARGE_M 4
+#endif
+  // fewer row blocks per workgroup while staging x costs little, more as M grows
+  if (M <= 2) launch_bl<W4A8_BL_RB_SMALL_M>(x, w, s, M, N, K, y, st);
+  else launch_bl<W4A8_BL_RB_LARGE_M>(x, w, s, M, N, K, y, st);
 }
 
 }  // namespace w4a8

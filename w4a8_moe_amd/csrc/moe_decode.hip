@@ -59,6 +59,9 @@ constexpr int kDepth = W4A8_DECODE_DEPTH;
 constexpr int kBody = W4A8_DECODE_BODY;                    // k-steps per unrolled loop body
 constexpr int kStageBatch = 4;                             // staging units in flight per thread
 static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
+// an LDS chunk holds at least one round of k-steps for the most column tiles (else the
+// chunk loop could not advance)
+static_assert(kDecodeLds / (32 * kDecodeMaxTiles) >= 128 * kDepth, "LDS chunk below one round");
 constexpr int kWeightLoadAux = W4A8_DECODE_NT_LOADS ? 2 : 0;   // cache-policy bits: nt
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
