@@ -57,7 +57,7 @@ namespace w4a8 {
 #endif
 constexpr int kDepth = W4A8_DECODE_DEPTH;
 constexpr int kBody = W4A8_DECODE_BODY;                    // k-steps per unrolled loop body
-constexpr int kStageBatch = 4;                             // staging units in flight per thread
+constexpr int kStageBatch = 8;                             // staging units in flight per thread
 static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
 // an LDS chunk holds at least one round of k-steps for the most column tiles (else the
 // chunk loop could not advance)
@@ -232,6 +232,19 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
     q0[d] = buf_ld16(wr, d < ST ? off0 + d * kTileBytes : kOutOfRange);
     q1[d] = buf_ld16(wr, d < ST1 ? off1 + d * kTileBytes : kOutOfRange);
   }
+  // Staging sources. A thread's staging slots all sit at lane tid % 64 of their 64-slot
+  // block, so it always stages column c = tid % 16 of a tile: the activation row behind
+  // column c of each tile is looked up once here (a byte offset into act, or out of range
+  // for a column past the expert's rows: the buffer load then returns zeros).
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)p.act, (short)0, (int)((GATEUP ? p.P / 2 : p.P) * p.K), 0x00020000);
+  uint32_t srow[MAXT];
+#pragma unroll
+  for (int j = 0; j < MAXT; ++j) {
+    const int col = j * 16 + (tid & 15);
+    const int r = GATEUP ? (p.sorted_pair[seg0 + min(col, cnt - 1)] >> 1) : seg0 + min(col, cnt - 1);
+    srow[j] = col < cnt ? (uint32_t)r * (uint32_t)p.K : kOutOfRange;
+  }
   int sg = 0;                                               // k-steps consumed so far
   for (int kc0 = k_begin; kc0 < k_end; kc0 += kc_max) {
     const int klen = min(kc_max, k_end - kc0);
@@ -245,25 +258,23 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
       // consecutive slots: no bank conflicts); slot v of the chunk is
       // (tile j, k-step st, sub-step m) = v / 64 and lane (c + 16 gg) = v % 64, which holds
       // codes 8 * (st*16 + gg*4 + m) .. +8 of token column j*16 + c. Batches of kStageBatch
-      // slots per thread issue all their global loads before waiting on the first.
+      // slots per thread issue all their loads (branch-free) before waiting on the first.
       const int slots = nt * S * 4 * 64;
       for (int v0 = 0; v0 < slots; v0 += kStageBatch * kDecodeWaves * kWave) {
-        int src[kStageBatch], kk[kStageBatch];
+        uint2 q[kStageBatch];
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
           const int v = v0 + b * kDecodeWaves * kWave + tid;
-          const int blk = v >> 6, l = v & 63;
+          const int blk = v >> 6;
           const int m = blk & 3, js = blk >> 2;
           const int j = js / S, st = js - j * S;
-          const int col = j * 16 + (l & 15);
-          kk[b] = st * 16 + (l >> 4) * 4 + m;
-          src[b] = (v < slots && col < cnt) ? (GATEUP ? (p.sorted_pair[seg0 + col] >> 1) : (seg0 + col)) : -1;
-        }
-        uint2 q[kStageBatch];
+          uint32_t base = srow[0];
 #pragma unroll
-        for (int b = 0; b < kStageBatch; ++b)
-          q[b] = src[b] >= 0 ? *reinterpret_cast<const uint2*>(p.act + (size_t)src[b] * p.K + kc0 + kk[b] * 8)
-                             : make_uint2(0, 0);
+          for (int jj = 1; jj < MAXT; ++jj) base = j == jj ? srow[jj] : base;
+          const uint32_t kk = (uint32_t)(st * 16 + ((tid & 63) >> 4) * 4 + m);
+          const uint32_t off = (v < slots && base != kOutOfRange) ? base + kc0 + kk * 8 : kOutOfRange;
+          q[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ar, off, 0, 0));
+        }
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
           const int v = v0 + b * kDecodeWaves * kWave + tid;
