@@ -377,22 +377,37 @@ void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st) {
 
 // ---------------------------------------------------------------------------- combine
 // out[t][n] = w0 * Y0 + w1 * Y1, Y = sum over split-K slices in slice order; fp32, then
-// bf16 (nearest even) or fp32. 4 channels per thread; a 1-D grid over (token, chunk).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ partial, int ksplit, int P, int H,
-                                                      const int32_t* __restrict__ pair_pos,
-                                                      const float* __restrict__ topk_w, int chunks,
-                                                      int out_bf16, void* __restrict__ out) {
+// bf16 (nearest even) or fp32. 4 channels per thread, 64 threads per workgroup (a few
+// MB of partials: many small workgroups), the slices' loads issued up to 8 at a time
+// before they are added (still in slice order).
+constexpr int kCombineThreads = 64;
+
+template <int BATCH>   // slices loaded per round: 1 for an unsplit reduction, else 8
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* __restrict__ partial, int ksplit, int P,
+                                                                 int H, const int32_t* __restrict__ pair_pos,
+                                                                 const float* __restrict__ topk_w, int chunks,
+                                                                 int out_bf16, void* __restrict__ out) {
   const int t = blockIdx.x / chunks;
-  const int n = ((blockIdx.x % chunks) * 256 + threadIdx.x) * 4;
+  const int n = ((blockIdx.x % chunks) * kCombineThreads + threadIdx.x) * 4;
   if (n >= H) return;
   const int r0 = pair_pos[2 * t], r1 = pair_pos[2 * t + 1];
   const float w0 = topk_w[2 * t], w1 = topk_w[2 * t + 1];
   float4 y0 = make_float4(0.f, 0.f, 0.f, 0.f), y1 = y0;
-  for (int s = 0; s < ksplit; ++s) {
-    const float4 a = *reinterpret_cast<const float4*>(partial + ((size_t)s * P + r0) * H + n);
-    const float4 b = *reinterpret_cast<const float4*>(partial + ((size_t)s * P + r1) * H + n);
-    y0.x += a.x; y0.y += a.y; y0.z += a.z; y0.w += a.w;
-    y1.x += b.x; y1.y += b.y; y1.z += b.z; y1.w += b.w;
+  for (int s0 = 0; s0 < ksplit; s0 += BATCH) {
+    float4 a[BATCH], b[BATCH];
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      const int s = min(s0 + u, ksplit - 1);              // in range; extra loads are not added
+      a[u] = *reinterpret_cast<const float4*>(partial + ((size_t)s * P + r0) * H + n);
+      b[u] = *reinterpret_cast<const float4*>(partial + ((size_t)s * P + r1) * H + n);
+    }
+#pragma unroll
+    for (int u = 0; u < BATCH; ++u) {
+      if (s0 + u < ksplit) {
+        y0.x += a[u].x; y0.y += a[u].y; y0.z += a[u].z; y0.w += a[u].w;
+        y1.x += b[u].x; y1.y += b[u].y; y1.z += b[u].z; y1.w += b[u].w;
+      }
+    }
   }
   float4 o;
   o.x = w0 * y0.x + w1 * y1.x;
@@ -411,9 +426,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 
 void launch_combine(const float* partial, int ksplit, int P, int H, const int32_t* pair_pos,
                     const float* topk_w, int T, bool out_bf16, void* out, hipStream_t st) {
-  const int chunks = (H / 4 + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((size_t)T * chunks)), dim3(256), 0, st, partial, ksplit, P, H,
-                     pair_pos, topk_w, chunks, out_bf16 ? 1 : 0, out);
+  const int chunks = (H / 4 + kCombineThreads - 1) / kCombineThreads;
+  const dim3 grid((unsigned)((size_t)T * chunks));
+  if (ksplit == 1)
+    hipLaunchKernelGGL(combine_kernel<1>, grid, dim3(kCombineThreads), 0, st, partial, ksplit, P, H, pair_pos, topk_w,
+                       chunks, out_bf16 ? 1 : 0, out);
+  else
+    hipLaunchKernelGGL(combine_kernel<8>, grid, dim3(kCombineThreads), 0, st, partial, ksplit, P, H, pair_pos, topk_w,
+                       chunks, out_bf16 ? 1 : 0, out);
 }
 
 }  // namespace w4a8
