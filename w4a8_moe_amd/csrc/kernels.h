@@ -48,7 +48,7 @@ struct MoeGemmParams {
   // down epilogue
   float* partial;              // [ksplit][P][H]
   // decode launch shape (set by plan_decode)
-  int kslice, ksplit, groups, lds_bytes, max_tiles;
+  int kslice, ksplit, groups, lds_bytes, max_tiles, waves;
 };
 
 #ifndef W4A8_DECODE_WAVES
@@ -57,7 +57,7 @@ struct MoeGemmParams {
 #ifndef W4A8_DECODE_LDS_KB
 #define W4A8_DECODE_LDS_KB 64
 #endif
-constexpr int kDecodeWaves = W4A8_DECODE_WAVES;   // waves per workgroup of the streaming kernel
+constexpr int kDecodeWaves = W4A8_DECODE_WAVES;   // most waves per workgroup of the streaming kernel
 constexpr int kDecodeMaxTiles = 4;                // 16-row column tiles per expert (64 rows)
 constexpr int kDecodeLds = W4A8_DECODE_LDS_KB * 1024;
 

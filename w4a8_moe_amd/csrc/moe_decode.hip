@@ -200,7 +200,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const int kc_max = ((p.lds_bytes / (32 * nt)) / (128 * kDepth)) * (128 * kDepth);   // fp16 rows of 16*nt tokens
 
   // weight row blocks of this wave: gate|up -> (cb, n_out/16 + cb); down -> (2cb, 2cb + 1)
-  const int cb = group * kDecodeWaves + wave;
+  const int nthr = blockDim.x;                              // p.waves waves
+  const int cb = group * p.waves + wave;
   const int blk0 = GATEUP ? cb : 2 * cb;
   const int blk1 = GATEUP ? (p.n_out / 16 + cb) : 2 * cb + 1;
   const bool has_work = blk0 * 16 < (GATEUP ? p.n_out : p.Nw);
@@ -260,11 +261,11 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
       // codes 8 * (st*16 + gg*4 + m) .. +8 of token column j*16 + c. Batches of kStageBatch
       // slots per thread issue all their loads (branch-free) before waiting on the first.
       const int slots = nt * S * 4 * 64;
-      for (int v0 = 0; v0 < slots; v0 += kStageBatch * kDecodeWaves * kWave) {
+      for (int v0 = 0; v0 < slots; v0 += kStageBatch * nthr) {
         uint2 q[kStageBatch];
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
-          const int v = v0 + b * kDecodeWaves * kWave + tid;
+          const int v = v0 + b * nthr + tid;
           const int blk = v >> 6;
           const int m = blk & 3, js = blk >> 2;
           const int j = js / S, st = js - j * S;
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
         }
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
-          const int v = v0 + b * kDecodeWaves * kWave + tid;
+          const int v = v0 + b * nthr + tid;
           if (v >= slots) break;
           // codes 4..7 of each 8 face the weights' high nibbles (16 q): staged divided by 16
           const uint4 w = make_uint4(cvt2_e4m3_f16<false>(q[b].x), cvt2_e4m3_f16<true>(q[b].x),
@@ -341,18 +342,53 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
 
 bool decode_fits(int T) { return T <= 16 * kDecodeMaxTiles; }
 
+// CUs of the current device (the streaming kernel holds two workgroups per CU).
+static int device_cus() {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  }
+  return cus[dev];
+}
+
+// Fraction of the workgroup slots busy over the rounds that `units` workgroups take.
+static double round_fill(long units, long slots) {
+  const long rounds = (units + slots - 1) / slots;
+  return rounds > 0 ? (double)units / (double)(rounds * slots) : 1.0;
+}
+
 void plan_decode(MoeGemmParams& p, bool gateup) {
   // an expert never holds more rows than there are tokens (its two slots differ)
   const int T = p.P / 2;
   p.max_tiles = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
   p.lds_bytes = kDecodeLds;
-  const int chans_per_wg = kDecodeWaves * (gateup ? 16 : 32);
-  p.groups = (p.n_out + chans_per_wg - 1) / chans_per_wg;
   if (gateup) {
-    p.kslice = p.K;                  // the fused epilogue needs the whole reduction
+    // The whole reduction (the fused epilogue needs it). Waves per workgroup (16 channels
+    // each): 8, or 7 when that fills the last round of workgroup slots (two per CU)
+    // better; a partly empty last round leaves HBM bandwidth unused. Mixtral-shaped
+    // I = 14336 = 7 * 2048: 7 waves give 1024 workgroups instead of 896 for 512 slots.
+    p.kslice = p.K;
     p.ksplit = 1;
+    const long experts = std::min(p.E, 2 * T);              // experts that can hold rows
+    const long slots = 2L * device_cus();
+    double best = -1.0;
+    for (int w = kDecodeWaves; w >= std::min(7, kDecodeWaves); --w) {
+      const int groups = (p.n_out + 16 * w - 1) / (16 * w);
+      const double fill = round_fill((long)groups * experts, slots);
+      if (fill > best + 1e-9) {
+        best = fill;
+        p.waves = w;
+        p.groups = groups;
+      }
+    }
   } else {
-    // one LDS chunk (fp16) per slice when an expert holds up to 16 rows
+    // split K: one LDS chunk (fp16) per slice when an expert holds up to 16 rows; more,
+    // shorter slices (to fill the last round) measured slower: more partial sums to add
+    p.waves = kDecodeWaves;
+    p.groups = (p.n_out + 32 * kDecodeWaves - 1) / (32 * kDecodeWaves);
     p.kslice = std::min(p.K, kDecodeLds / 32);
     p.ksplit = (p.K + p.kslice - 1) / p.kslice;
   }
@@ -361,7 +397,7 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
 template <bool GATEUP>
 static void launch_decode_t(const MoeGemmParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)(p.groups * p.ksplit * p.E);
-  const dim3 block(kDecodeWaves * kWave);
+  const dim3 block(p.waves * kWave);
   if (p.max_tiles <= 1)
     hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 1>), dim3(grid), block, p.lds_bytes, st, p);
   else if (p.max_tiles == 2)
