@@ -2,8 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one forward of the layer over one batch of synthetic tokens: moe_route_sort,
-fp8_quant_static (x -> E4M3), moe_gemm1_w4a8, moe_gemm2_w4a8 (down + combine). Inputs
+A step is one forward of the layer over one batch of synthetic tokens:
+moe_route_sort_quant (routing and x -> E4M3 in one call), moe_gemm1_w4a8,
+moe_gemm2_w4a8 (down + combine); four consecutive steps are captured in one HIP graph,
+as a model's decode graph holds its consecutive layers, and exactly K steps are timed. Inputs
 (packed weights, scales, x, logits) are resident in HBM before the timed region. The
 packed weights are rotated over several copies when one copy would fit in the 256 MB
 Infinity Cache, so that the HBM stream is measured. w4_pack + w4_tile (load time) and the block-FP8
@@ -53,6 +55,8 @@ def static_scales(name):
 def bf16_dev(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
+
+STEPS_PER_GRAPH = 4      # consecutive layer steps captured in one HIP graph
 
 COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_prefill": "moe_prefill_grok_T32768.json"}
 
@@ -190,11 +194,8 @@ def measure_layer(torch, W, cfg, steps, warmup):
     ro = W.route_outputs(T, E, dev)
     od = "f32" if cfg.out_f32 else "bf16"
 
-    def route():
-        W.moe_route_sort(logits, out=ro)
-
-    def quant():
-        W.fp8_quant_static(x, s_x, out=xq)
+    def route_quant():
+        W.moe_route_sort_quant(logits, x, s_x, out=ro, xq=xq)
 
     def gemm1(i):
         W.moe_gemm1_w4a8(xq, s_x, W13[i % copies], s13, ro["offsets"], ro["sorted_pair"], cfg.act, s_a, ws=ws1,
@@ -205,34 +206,46 @@ def measure_layer(torch, W, cfg, steps, warmup):
                          out=out)
 
     def step(i):
-        route(); quant(); gemm1(i); gemm2(i)
+        route_quant(); gemm1(i); gemm2(i)
 
-    # eager reference step, then one captured HIP graph per weight copy (launch overhead
-    # of the Python binding stays out of the timed region); the replay must match eager
+    # eager reference step, then captured HIP graphs (launch overhead of the Python binding
+    # stays out of the timed region): per weight copy, one of a single step and one of
+    # STEPS_PER_GRAPH consecutive steps (the weight copies alternating inside), as a model's
+    # decode graph holds its consecutive layers; every replay must match the eager step
     step(0)
     torch.cuda.synchronize()
     ref_out = out.clone()
     counts = ro["counts"].cpu().numpy()
     ids = ro["ids"].cpu().numpy()
-    graphs = []
+    graphs1, graphsN = [], []
     for c in range(copies):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step(c)
-        graphs.append(g)
+        for n, dst in ((1, graphs1), (STEPS_PER_GRAPH, graphsN)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for k in range(n):
+                    step(c + k)
+            dst.append(g)
     for i in range(warmup):
-        graphs[i % copies].replay()
+        graphs1[i % copies].replay()
     torch.cuda.synchronize()
-    graphs[0].replay()
-    torch.cuda.synchronize()
-    if not torch.equal(out, ref_out):
-        raise RuntimeError("graph replay differs from the eager step")
+    for g in (graphs1[0], graphsN[0]):
+        out.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(out, ref_out):
+            raise RuntimeError("graph replay differs from the eager step")
 
-    # ---- timed region: K steps, wall clock between two synchronizations
+    # ---- timed region: exactly K steps (graphs of STEPS_PER_GRAPH steps, single-step
+    #      graphs for the remainder), wall clock between two synchronizations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        graphs[i % copies].replay()
+    done = 0
+    while done + STEPS_PER_GRAPH <= steps:
+        graphsN[done % copies].replay()
+        done += STEPS_PER_GRAPH
+    while done < steps:
+        graphs1[done % copies].replay()
+        done += 1
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / steps
@@ -252,7 +265,7 @@ def measure_layer(torch, W, cfg, steps, warmup):
         torch.cuda.synchronize()
         return ev0.elapsed_time(ev1) * 1e3 / n
 
-    per_call = {"route_sort": per_launch_us(lambda i: route()), "quant_x": per_launch_us(lambda i: quant()),
+    per_call = {"route_sort_quant": per_launch_us(lambda i: route_quant()),
                 "gemm1": per_launch_us(gemm1), "gemm2_combine": per_launch_us(gemm2)}
     layer_bytes, gemm1_bytes, touched = moe_bytes(cfg, counts)
     layer_us = ms_per_step * 1e3
@@ -288,7 +301,8 @@ def measure_layer(torch, W, cfg, steps, warmup):
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": 2,
                    "activation": ACT_NAMES[cfg.act], "out": "fp32" if cfg.out_f32 else "bf16",
-                   "weight_copies_rotated": copies, "experts_touched": touched},
+                   "weight_copies_rotated": copies, "experts_touched": touched,
+                   "steps_per_graph": STEPS_PER_GRAPH},
         **layer_frac,
         "layer_bytes": int(layer_bytes),
         "calls_us": {k: round(v, 2) for k, v in per_call.items()},

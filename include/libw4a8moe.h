@@ -148,6 +148,24 @@ int32_t moe_route_sort(const float* logits, int32_t T, int32_t E,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_route_sort_quant -- moe_route_sort and fp8_quant_static of the layer's input in one
+ * call: the per-token work that precedes the grouped GEMMs (same passages). Up to 256
+ * tokens both run in a single launch (the quantization in extra workgroups beside the
+ * routing one); above, the routing kernels and then the quantization.
+ *
+ *   logits .. pair_pos, ws, ws_bytes  exactly as moe_route_sort
+ *   x_bf16  [T][H] bf16;  s_x its static scale (finite, > 0)
+ *   x_e4m3  [T][H] (out) the same bytes fp8_quant_static(x_bf16, T*H, s_x) writes
+ * Requires what moe_route_sort requires, H >= 1, T*H < 2^31; x_bf16 and x_e4m3 16-byte
+ * aligned when T > 0.
+ */
+int32_t moe_route_sort_quant(const float* logits, int32_t T, int32_t E,
+                             int32_t* topk_ids, float* topk_w, int32_t* counts, int32_t* offsets,
+                             int32_t* sorted_pair, int32_t* pair_pos,
+                             const uint16_t* x_bf16, int32_t H, float s_x, uint8_t* x_e4m3,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/*
  * moe_gemm1_w4a8 -- gate|up grouped GEMM of the routed experts with int4 weights
  * upcast to fp8 in registers, fp8 MFMA with fp32 accumulation, fused gated
  * activation and static fp8 requantization ("INT4 MoE weights, FP8 compute",

@@ -17,7 +17,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = W.header_functions()
-    assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
+    assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_route_sort_quant", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
                           "fp8_block_quant", "fp8_block_linear", "w4a8_workspace_bytes", "w4a8_status_str",
                           "w4a8_moe_kernel"}
     for n in names:
@@ -34,6 +34,22 @@ def test_status_strings(L):
     for code in (0, -1, -2, -3, -4, -5, -6, -7):
         assert W.status_str(code) and W.status_str(code) != "unknown status"
     assert W.status_str(-99) == "unknown status"
+
+
+def test_route_sort_quant_validation(L):
+    def call(T=32, E=8, H=256, s=0.5, logits=A, x=A, xq=A, ws=None, nws=0):
+        return L.moe_route_sort_quant(logits, T, E, A, A, A, A, A, A, x, H, s, xq, ws, nws, None)
+    assert call(T=-1) == W.ERR_SHAPE
+    assert call(E=1) == W.ERR_SHAPE
+    assert call(H=0) == W.ERR_SHAPE
+    assert call(T=1 << 20, H=4096) == W.ERR_SHAPE              # T*H >= 2^31
+    assert call(s=0.0) == W.ERR_ARG
+    assert call(s=float("inf")) == W.ERR_ARG
+    assert call(x=None) == W.ERR_NULL
+    assert call(xq=None) == W.ERR_NULL
+    assert call(x=U) == W.ERR_ALIGN
+    assert call(xq=U) == W.ERR_ALIGN
+    assert call(T=300) == W.ERR_WORKSPACE                      # several blocks need a workspace
 
 
 def test_w4_tile_validation(L):

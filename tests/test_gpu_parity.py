@@ -100,6 +100,24 @@ def test_route_sort_bit_exact(T, E, sigma):
     _check_route((rng.standard_normal((T, E)) * sigma).astype(np.float32))
 
 
+@pytest.mark.parametrize("T,E,H", [(32, 8, 4096), (1, 2, 136), (256, 8, 520), (257, 8, 264), (3, 16, 9), (0, 8, 64)])
+def test_route_sort_quant_matches_separate_calls(T, E, H):
+    """One launch (T <= 256) or the multi-kernel routing then the quantization: the same
+    bytes as moe_route_sort and fp8_quant_static called apart (ragged T*H % 8 tails too)."""
+    rng = np.random.default_rng(T * 3 + E + H)
+    logits = f32_dev((rng.standard_normal((T, E)) * 1.5).astype(np.float32))
+    x = bf16_dev(synth.f32_to_bf16_bits((rng.standard_normal((T, H)) * 2).astype(np.float32)))
+    s_x = np.float32(0.0123)
+    got = W.moe_route_sort_quant(logits, x, s_x)
+    ref = W.moe_route_sort(logits)
+    for k in ("ids", "weights", "counts", "offsets", "sorted_pair", "pair_pos"):
+        assert torch().equal(got[k], ref[k]), k
+    assert torch().equal(got["xq"], W.fp8_quant_static(x, s_x))
+    if T:
+        assert same_codes(host(got["xq"]).reshape(-1),
+                          oracle.quantize_static(oracle.bf16_to_f32(host(x).reshape(-1)), s_x)).all()
+
+
 def test_route_sort_empty_and_ties():
     _check_route(np.zeros((0, 8), np.float32))
     l = np.array([[1, 2, 2, 0.5], [0, 0, 0, 0], [3, 1, 3, 3], [-1, 5, -1, -1], [7, 7, 7, 7]], np.float32)

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "w4_tile": (_I32, [_P, _I32, _I32, _I32, _P, _P]),
     "fp8_quant_static": (_I32, [_P, _I64, _F32, _P, _P]),
     "moe_route_sort": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_route_sort_quant": (_I32, [_P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _I32, _F32, _P, _P, _SZ, _P]),
     "moe_gemm1_w4a8": (_I32, [_P, _I32, _F32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
                               _P, _SZ, _P]),
     "moe_gemm2_w4a8": (_I32, [_P, _F32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
@@ -199,6 +200,31 @@ def moe_route_sort(logits, out=None):
     return o
 
 
+def moe_route_sort_quant(logits, x, s_x, out=None, xq=None):
+    """moe_route_sort(logits) and fp8_quant_static(x, s_x) in one call (one launch up to
+    256 tokens): the dict of moe_route_sort plus "xq", the E4M3 codes of x."""
+    torch = _torch()
+    T, E = logits.shape
+    H = x.shape[1]
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(x, torch.bfloat16, (T, H), "x")
+    dev = logits.device
+    o = out if out is not None else route_outputs(T, E, dev)
+    if xq is None:
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+    _need(xq, torch.uint8, (T, H), "xq")
+    ids, w, counts, offsets, sp, pos, ws = (o["ids"], o["weights"], o["counts"], o["offsets"], o["sorted_pair"],
+                                            o["pair_pos"], o["ws"])
+    if ws.numel() < workspace_bytes(OP_ROUTE_SORT, T, 0, 0, E):
+        raise ValueError("route workspace too small")
+    _check("moe_route_sort_quant",
+           lib().moe_route_sort_quant(_ptr(logits), T, E, _ptr(ids), _ptr(w), _ptr(counts), _ptr(offsets), _ptr(sp),
+                                      _ptr(pos), _ptr(x), H, float(s_x), _ptr(xq), _ptr(ws), ws.numel(),
+                                      _stream(dev)))
+    o["xq"] = xq
+    return o
+
+
 def moe_gemm1_w4a8(x, s_x, w13, s_w13, offsets, sorted_pair, act, s_a, debug=False, ws=None, out=None):
     """x bf16 [T, H] or uint8 E4M3 codes [T, H]; returns a_fp8 uint8 [2T, I] (and fp32 [2T, 2I] if debug)."""
     torch = _torch()
@@ -282,6 +308,10 @@ def fp8_block_linear(x, w, s, out=None):
 def moe_layer(x, s_x, logits, w13, s_w13, w2, s_w2, act, s_a, out_dtype="bf16"):
     """The whole layer: route+sort, gate|up, down+combine (x bf16 or E4M3 codes; w13 and w2
     in the tiled layout)."""
-    r = moe_route_sort(logits)
+    if x.dtype == _torch().bfloat16:
+        r = moe_route_sort_quant(logits, x, s_x)
+        x = r["xq"]
+    else:
+        r = moe_route_sort(logits)
     a = moe_gemm1_w4a8(x, s_x, w13, s_w13, r["offsets"], r["sorted_pair"], act, s_a)
     return moe_gemm2_w4a8(a, s_a, w2, s_w2, r["offsets"], r["pair_pos"], r["weights"], out_dtype)

@@ -142,6 +142,29 @@ int32_t moe_route_sort(const float* logits, int32_t T, int32_t E, int32_t* topk_
   return launch_status();
 }
 
+int32_t moe_route_sort_quant(const float* logits, int32_t T, int32_t E, int32_t* topk_ids, float* topk_w,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                             const uint16_t* x_bf16, int32_t H, float s_x, uint8_t* x_e4m3, void* ws,
+                             size_t ws_bytes, void* stream) {
+  if (T < 0 || T > kMaxRouteTokens || E < 2 || E > W4A8_MAX_EXPERTS || H < 1) return W4A8_ERR_SHAPE;
+  if ((int64_t)T * H >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;
+  if (!good_scale(s_x)) return W4A8_ERR_ARG;
+  if (!counts || !offsets) return W4A8_ERR_NULL;
+  if (T > 0 && (!logits || !topk_ids || !topk_w || !sorted_pair || !pair_pos || !x_bf16 || !x_e4m3))
+    return W4A8_ERR_NULL;
+  if (!aligned16(counts) || !aligned16(offsets)) return W4A8_ERR_ALIGN;
+  if (T > 0 && (!aligned16(logits) || !aligned16(topk_ids) || !aligned16(topk_w) || !aligned16(sorted_pair) ||
+                !aligned16(pair_pos) || !aligned16(x_bf16) || !aligned16(x_e4m3)))
+    return W4A8_ERR_ALIGN;
+  const size_t need = w4a8_workspace_bytes(W4A8_OP_ROUTE_SORT, T, 0, 0, E);
+  if (ws_bytes < need) return W4A8_ERR_WORKSPACE;
+  if (need > 0 && !ws) return W4A8_ERR_NULL;
+  if (need > 0 && !aligned16(ws)) return W4A8_ERR_ALIGN;
+  launch_route_sort(logits, T, E, topk_ids, topk_w, counts, offsets, sorted_pair, pair_pos, ws, as_stream(stream),
+                    T > 0 ? x_bf16 : nullptr, (int64_t)T * H, s_x, x_e4m3);
+  return launch_status();
+}
+
 int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x, const int32_t* w13, const float* s_w13,
                        const int32_t* offsets, const int32_t* sorted_pair, int32_t T, int32_t H, int32_t I,
                        int32_t E, int32_t act, float s_a, uint8_t* a_fp8, float* gateup_dbg, void* ws,

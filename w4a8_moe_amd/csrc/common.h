@@ -120,4 +120,29 @@ __device__ __forceinline__ void lds_barrier() {
 __device__ __forceinline__ int wave_id() { return threadIdx.x / kWave; }
 __device__ __forceinline__ int lane_id() { return threadIdx.x % kWave; }
 
+// fp8_quant_static's arithmetic: e4m3(fp32(x / s)) (correctly rounded quotient, nearest
+// even, saturated) over n bf16 elements, 8 per thread and round: groups [8 i, 8 i + 8) for
+// i = first, first + stride, ... < n / 8, then the n % 8 tail by threads first < 8. Every
+// caller runs this same code, so the codes are the same bytes wherever x is quantized.
+__device__ __forceinline__ uint32_t quant4_e4m3(uint32_t lo, uint32_t hi, float s) {
+  return pack4_e4m3(bf16_bits_to_f32(lo & 0xFFFFu) / s, bf16_bits_to_f32(lo >> 16) / s,
+                    bf16_bits_to_f32(hi & 0xFFFFu) / s, bf16_bits_to_f32(hi >> 16) / s);
+}
+
+__device__ __forceinline__ void fp8_quant_span(const uint16_t* __restrict__ x, int64_t n, float s,
+                                               uint8_t* __restrict__ out, int64_t first, int64_t stride) {
+  const int64_t n8 = n >> 3;
+  const uint4* src = reinterpret_cast<const uint4*>(x);
+  uint2* dst = reinterpret_cast<uint2*>(out);
+  for (int64_t i = first; i < n8; i += stride) {
+    const uint4 v = src[i];
+    dst[i] = make_uint2(quant4_e4m3(v.x, v.y, s), quant4_e4m3(v.z, v.w, s));
+  }
+  const int64_t t = n8 * 8 + first;                         // the tail: one element per thread
+  if (t < n && first < 8) {
+    const uint32_t c = pack4_e4m3(bf16_bits_to_f32(x[t]) / s, 0.f, 0.f, 0.f);
+    out[t] = (uint8_t)(c & 0xFFu);
+  }
+}
+
 }  // namespace w4a8

@@ -18,12 +18,16 @@ constexpr uint32_t kTileBytes = 1024;
 void launch_w4_pack(const uint16_t* w, int64_t rows, int K, int32_t* packed, float* scale, hipStream_t st);
 void launch_w4_tile(const int32_t* packed, int64_t E, int N, int K, int32_t* tiled, hipStream_t st);
 void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st);
+int fp8_quant_blocks(int64_t n);      // 256-thread workgroups of one quantization launch
 void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st);
 
 // ---- route.hip
 size_t route_workspace_bytes(int T, int E);
+// with x (T*H bf16, xn elements): also xq = fp8_quant_static(x, s_x), in the same launch
+// when the routing is one workgroup
 void launch_route_sort(const float* logits, int T, int E, int32_t* ids, float* tw, int32_t* counts,
-                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st);
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st,
+                       const uint16_t* x = nullptr, int64_t xn = 0, float s_x = 1.0f, uint8_t* xq = nullptr);
 
 // ---- moe_decode.hip / moe_prefill.hip: grouped GEMM of the routed experts
 // One description serves both GEMMs:

@@ -95,35 +95,20 @@ void launch_w4_tile(const int32_t* packed, int64_t E, int N, int K, int32_t* til
 }
 
 // -------------------------------------------------------------------- fp8_quant_static
-// 8 elements per thread per iteration (16 B in, 8 B out); a grid-stride loop.
-__device__ __forceinline__ uint32_t quant4(uint32_t lo, uint32_t hi, float s) {
-  return pack4_e4m3(bf16_bits_to_f32(lo & 0xFFFFu) / s, bf16_bits_to_f32(lo >> 16) / s,
-                    bf16_bits_to_f32(hi & 0xFFFFu) / s, bf16_bits_to_f32(hi >> 16) / s);
-}
-
+// 8 elements per thread per iteration (16 B in, 8 B out); a grid-stride loop
+// (fp8_quant_span, shared with the routing launch that quantizes x alongside).
 __global__ __launch_bounds__(256) void fp8_quant_kernel(const uint16_t* __restrict__ x, int64_t n, float s,
                                                         uint8_t* __restrict__ out) {
-  const int64_t n8 = n >> 3;
-  const uint4* src = reinterpret_cast<const uint4*>(x);
-  uint2* dst = reinterpret_cast<uint2*>(out);
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8; i += (int64_t)gridDim.x * blockDim.x) {
-    uint4 v = src[i];
-    dst[i] = make_uint2(quant4(v.x, v.y, s), quant4(v.z, v.w, s));
-  }
-  // tail (n % 8 elements): one thread each
-  const int64_t t = n8 * 8 + blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-  if (t < n && t < n8 * 8 + 8) {
-    uint32_t c = pack4_e4m3(bf16_bits_to_f32(x[t]) / s, 0.f, 0.f, 0.f);
-    out[t] = (uint8_t)(c & 0xFFu);
-  }
+  fp8_quant_span(x, n, s, out, blockIdx.x * (int64_t)blockDim.x + threadIdx.x, (int64_t)gridDim.x * blockDim.x);
+}
+
+int fp8_quant_blocks(int64_t n) {
+  const int64_t blocks = ((n >> 3) + 255) / 256;
+  return (int)std::min<int64_t>(std::max<int64_t>(blocks, 1), 8192);
 }
 
 void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st) {
-  const int64_t n8 = n >> 3;
-  int64_t blocks = (n8 + 255) / 256;
-  if (blocks < 1) blocks = 1;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(fp8_quant_kernel, dim3((unsigned)blocks), dim3(256), 0, st, x, n, s, out);
+  hipLaunchKernelGGL(fp8_quant_kernel, dim3((unsigned)fp8_quant_blocks(n)), dim3(256), 0, st, x, n, s, out);
 }
 
 // ---------------------------------------------------------------- fp8_block_quant
@@ -160,7 +145,7 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const uint16_t* __
     const int c = c0 + 8 * i;
     if (c >= K) break;
     uint2 o = make_uint2(0, 0);
-    if (s != 0.0f) o = make_uint2(quant4(v[i].x, v[i].y, s), quant4(v[i].z, v[i].w, s));
+    if (s != 0.0f) o = make_uint2(quant4_e4m3(v[i].x, v[i].y, s), quant4_e4m3(v[i].z, v[i].w, s));
     *reinterpret_cast<uint2*>(q + (size_t)r * K + c) = o;
   }
 }

@@ -57,11 +57,18 @@ __device__ __forceinline__ void wave_ranks(bool valid, int i0, int i1, int E, in
   }
 }
 
-// Single-block path (T <= 256): everything in one launch, no workspace.
+// Single-block path (T <= 256): everything in one launch, no workspace. Workgroups past
+// the first, when there are any, quantize x to E4M3 (fp8_quant_static's code) meanwhile.
 __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
     const float* __restrict__ logits, int T, int E, int32_t* __restrict__ ids, float* __restrict__ tw,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_pair,
-    int32_t* __restrict__ pair_pos) {
+    int32_t* __restrict__ pair_pos, const uint16_t* __restrict__ x, int64_t xn, float s_x,
+    uint8_t* __restrict__ xq) {
+  if (blockIdx.x > 0) {
+    fp8_quant_span(x, xn, s_x, xq, (blockIdx.x - 1) * (int64_t)kRouteThreads + threadIdx.x,
+                   (int64_t)(gridDim.x - 1) * kRouteThreads);
+    return;
+  }
   extern __shared__ int smem[];
   int* wt = smem;                              // [waves][E]
   int* off = smem + kRouteWaves * E;           // [E+1]
@@ -172,13 +179,17 @@ size_t route_workspace_bytes(int T, int E) {
 }
 
 void launch_route_sort(const float* logits, int T, int E, int32_t* ids, float* tw, int32_t* counts,
-                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st) {
+                       int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws, hipStream_t st,
+                       const uint16_t* x, int64_t xn, float s_x, uint8_t* xq) {
   if (T <= kRouteThreads) {
+    // with x: the quantization rides along in extra workgroups of the same launch
+    const unsigned grid = 1 + (x && xn > 0 ? (unsigned)fp8_quant_blocks(xn) : 0u);
     const size_t lds = (size_t)(kRouteWaves * E + E + 1) * sizeof(int);
-    hipLaunchKernelGGL(route_small_kernel, dim3(1), dim3(kRouteThreads), lds, st, logits, T, E, ids, tw,
-                       counts, offsets, sorted_pair, pair_pos);
+    hipLaunchKernelGGL(route_small_kernel, dim3(grid), dim3(kRouteThreads), lds, st, logits, T, E, ids, tw,
+                       counts, offsets, sorted_pair, pair_pos, x, xn, s_x, xq);
     return;
   }
+  if (x && xn > 0) launch_fp8_quant(x, xn, s_x, xq, st);
   const int nb = (T + kRouteThreads - 1) / kRouteThreads;
   int32_t* cnt = static_cast<int32_t*>(ws);
   int32_t* base = cnt + (size_t)nb * E;
