@@ -58,6 +58,10 @@ constexpr uint32_t kPOutOfRange = 0x80000000u;   // past every buffer (all are <
 __device__ __forceinline__ uint4 pf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
+// per-lane offset plus a wave-uniform one (the step), added by the load itself
+__device__ __forceinline__ uint4 pf_ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 0));
+}
 
 // Four two's-complement nibbles (sel = nibble & 7 per byte, sgn = 4 * sign bit per byte)
 // -> four exact E4M3 codes: 0..7 -> 00 38 40 44 48 4A 4C 4E, -8..-1 -> D0 CE CC CA C8 C4
@@ -194,7 +198,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   uint4 tq[kTJ];
   auto load_tokens = [&](int s) {
 #pragma unroll
-    for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16(tr, toff[j] + (uint32_t)(s * 128));
+    for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16s(tr, toff[j], (uint32_t)(s * 128));
   };
   auto store_tokens = [&](int buf) {
 #pragma unroll
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   uint4 w0[4], w1[4];          // raw weights of steps s and s+1
   auto load_weights = [&](uint4 (&w)[4], int s) {
 #pragma unroll
-    for (int a = 0; a < 4; ++a) w[a] = pf_ld16(wr, woff[a] + (uint32_t)(s * kTileBytes));
+    for (int a = 0; a < 4; ++a) w[a] = pf_ld16s(wr, woff[a], (uint32_t)(s * kTileBytes));
   };
 
   // ---- prologue: weights of steps 0..2 in flight, tokens of step 0 in LDS, of step 1 in flight
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
       if ((bb & 1) == 0)
         *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                     // step s+1
       else
-        tq[j] = pf_ld16(tr, toff[j] + (uint32_t)((s + 2) * 128));             // step s+2
+        tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((s + 2) * 128));             // step s+2
 #pragma unroll
       for (int wi = bb; wi < 16; wi += kTB) {
         const int a = wi >> 2, tw = wi & 3;
@@ -257,7 +261,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
       }
       // words wi are converted at bb = wi (16 blocks): block a's last word goes at bb = 4 a + 3
       static_assert(kTB == 16, "the reload points below follow the conversion order for 16 blocks");
-      if ((bb & 3) == 3) w1[bb >> 2] = pf_ld16(wr, woff[bb >> 2] + (uint32_t)((s + 2) * kTileBytes));
+      if ((bb & 3) == 3) w1[bb >> 2] = pf_ld16s(wr, woff[bb >> 2], (uint32_t)((s + 2) * kTileBytes));
       __builtin_amdgcn_sched_barrier(0);
       if (bb < kTB - 1) bcur = bnext;
     }
