@@ -112,8 +112,12 @@ __device__ __forceinline__ uint32_t word_of(const uint4& q, int m) {
 // loads, which would make the compiler drain every outstanding load before each use).
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
-__device__ __forceinline__ uint4 buf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kWeightLoadAux));
+// A lane's fixed offset plus the k-step's (a wave-uniform scalar, added by the load): no
+// per-lane arithmetic per load. Past the wave's K-range the scalar part is kOutOfRange.
+__device__ __forceinline__ uint4 buf_ld16_step(__amdgpu_buffer_rsrc_t r, uint32_t voff, int step, int steps) {
+  const uint32_t soff = step < steps ? (uint32_t)step * kTileBytes : kOutOfRange;
+  return __builtin_bit_cast(
+      uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), kWeightLoadAux));
 }
 
 
@@ -148,8 +152,8 @@ __device__ __forceinline__ void stream_step(uint4& q0, uint4& q1, __amdgpu_buffe
   mma_step<NT>(q0, q1, lds, s, S, nt, lane, mlo, mhi, acc0, acc1);
   __builtin_amdgcn_sched_barrier(0);                        // keep the refill after the use
   const int nxt = gstep + kDepth;
-  q0 = buf_ld16(wr, nxt < ST ? off0 + nxt * kTileBytes : kOutOfRange);
-  q1 = buf_ld16(wr, nxt < ST1 ? off1 + nxt * kTileBytes : kOutOfRange);
+  q0 = buf_ld16_step(wr, off0, nxt, ST);
+  q1 = buf_ld16_step(wr, off1, nxt, ST1);
 }
 
 // The S k-steps of one LDS chunk against the column tiles (see mma_step). Full rounds of
@@ -230,8 +234,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   uint4 q0[kDepth], q1[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
-    q0[d] = buf_ld16(wr, d < ST ? off0 + d * kTileBytes : kOutOfRange);
-    q1[d] = buf_ld16(wr, d < ST1 ? off1 + d * kTileBytes : kOutOfRange);
+    q0[d] = buf_ld16_step(wr, off0, d, ST);
+    q1[d] = buf_ld16_step(wr, off1, d, ST1);
   }
   // Staging sources. A thread's staging slots all sit at lane tid % 64 of their 64-slot
   // block, so it always stages column c = tid % 16 of a tile: the activation row behind
