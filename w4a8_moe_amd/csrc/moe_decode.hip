@@ -126,12 +126,19 @@ __device__ __forceinline__ uint4 buf_ld16_step(__amdgpu_buffer_rsrc_t r, uint32_
 template <int NT>
 __device__ __forceinline__ void mma_step(const uint4& a0, const uint4& a1, const uint8_t* lds, int s, int S, int nt,
                                          int lane, uint32_t mlo, uint32_t mhi, v4f* acc0, v4f* acc1) {
+  // tile 0's four B operands are read first (their latency runs under the conversions)
+  v8h b0[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+    b0[m] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(lds + (s * 4 + m) * 1024 + lane * 16));
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const v8h A0 = int4x8_to_f16(word_of(a0, m), mlo, mhi);
     const v8h A1 = int4x8_to_f16(word_of(a1, m), mlo, mhi);
+    acc0[0] = mfma_f16(A0, b0[m], acc0[0]);
+    acc1[0] = mfma_f16(A1, b0[m], acc1[0]);
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int j = 1; j < NT; ++j) {
       if (j < nt) {
         const v8h b = __builtin_bit_cast(
             v8h, *reinterpret_cast<const uint4*>(lds + ((j * S + s) * 4 + m) * 1024 + lane * 16));
