@@ -74,12 +74,24 @@ GROK_DECODE = MoEConfig("grok_decode", T=32, H=6144, I=32768, E=8, act=ACT_GELU_
 GROK_PREFILL = MoEConfig("grok_prefill", T=32768, H=6144, I=32768, E=8, act=ACT_GELU_ERF,
                          w_sigma=0.015, logit_sigma=1.5, out_f32=False, w_cfg=3, x_cfg=4,
                          expert_bias=True)
+# One GPU's share of the Grok-1 layer under 8-way tensor parallelism (the page "ROCm:
+# enable trillion-parameter MoE models with INT4-FP8 single node" serves it with --tp 8):
+# each GPU holds I / 8 = 4096 gate and up channels and the matching K-slice of the down
+# projection, while routing is replicated, so the tokens and router logits are those of
+# the full layer (same activation seeds). The weights are a layer of their own with the
+# share's shape (seed 6).
+GROK_TP8_DECODE = MoEConfig("grok_tp8_decode", T=32, H=6144, I=4096, E=8, act=ACT_GELU_ERF,
+                            w_sigma=0.015, logit_sigma=1.5, out_f32=False, w_cfg=6, x_cfg=3)
+GROK_TP8_PREFILL = MoEConfig("grok_tp8_prefill", T=32768, H=6144, I=4096, E=8, act=ACT_GELU_ERF,
+                             w_sigma=0.015, logit_sigma=1.5, out_f32=False, w_cfg=6, x_cfg=4,
+                             expert_bias=True)
 BLOCK_QKVZ_M1 = BlockConfig("block_qkvz_m1", M=1, N=16384, K=2560, sub=0)
 BLOCK_QKVZ_M8 = BlockConfig("block_qkvz_m8", M=8, N=16384, K=2560, sub=0)
 BLOCK_QKV_M1 = BlockConfig("block_qkv_m1", M=1, N=13312, K=2560, sub=1)
 BLOCK_QKV_M8 = BlockConfig("block_qkv_m8", M=8, N=13312, K=2560, sub=1)
 
-MOE_CONFIGS = {c.name: c for c in (TINY, MIXTRAL_DECODE, GROK_DECODE, GROK_PREFILL)}
+MOE_CONFIGS = {c.name: c for c in (TINY, MIXTRAL_DECODE, GROK_DECODE, GROK_PREFILL, GROK_TP8_DECODE,
+                                   GROK_TP8_PREFILL)}
 BLOCK_CONFIGS = {c.name: c for c in (BLOCK_QKVZ_M1, BLOCK_QKVZ_M8, BLOCK_QKV_M1, BLOCK_QKV_M8)}
 
 

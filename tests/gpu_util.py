@@ -75,6 +75,7 @@ def assert_final_close(out_gpu, out_ref):
     d = np.abs(out_gpu - out_ref)
     assert d.max() <= 1e-2 * m, f"max err {d.max():.4g} > 1e-2 * {m:.4g}"
     frac = np.mean(d > 1e-3 * m)
+    print(f"final: max |err| / max|ref| = {d.max() / m:.3g}, {frac:.4%} of {d.size} elements above 1e-3 max|ref|")
     assert frac <= 1e-3, f"{frac:.4%} of elements above 1e-3 max|ref|"
 
 
