@@ -27,9 +27,11 @@
 // projection erred by 5e-6 of its largest output instead of 1e-8.)
 //
 // Mapping. A workgroup = 8 waves on one expert and one K-slice. The activation rows of
-// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS widened
-// to fp16, in the order the MFMA B operand is read (one ds_read_b128 per lane and
-// instruction, 1 KB per wave without bank conflicts). Each wave owns two blocks of 16
+// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS as their
+// E4M3 bytes (16 rows x 4096 K in 64 KB, so up to 16 rows the whole reduction of
+// Mixtral's gate|up is one chunk, with no restaging barrier mid-stream), in the order the
+// MFMA B operand is read (one ds_read_b128 per lane covers two instructions, 1 KB per
+// wave without bank conflicts), and widened to fp16 in registers. Each wave owns two blocks of 16
 // weight rows (gate rows n..n+15 and up rows I+n..I+n+15, or two blocks of down rows) and
 // streams them with 16-byte buffer loads, kDepth k-steps (of 128) ahead, without a break
 // at LDS chunk boundaries. The weights are in the tiled layout (w4_tile): one load
@@ -61,7 +63,7 @@ constexpr int kStageBatch = 8;                             // staging units in f
 static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
 // an LDS chunk holds at least one round of k-steps for the most column tiles (else the
 // chunk loop could not advance)
-static_assert(kDecodeLds / (32 * kDecodeMaxTiles) >= 128 * kDepth, "LDS chunk below one round");
+static_assert(kDecodeLds / (16 * kDecodeMaxTiles) >= 128 * kDepth, "LDS chunk below one round");
 constexpr int kWeightLoadAux = W4A8_DECODE_NT_LOADS ? 2 : 0;   // cache-policy bits: nt
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 
@@ -121,27 +123,39 @@ __device__ __forceinline__ uint4 buf_ld16_step(__amdgpu_buffer_rsrc_t r, uint32_
 }
 
 
+// 8 E4M3 codes (one 8-byte half of a 16-byte LDS slot) -> the fp16 B operand of one
+// MFMA, exact; codes 4..7 face the weights' high nibbles (16 q) and are divided by 16
+// (E4M3 keeps 3 mantissa bits, so the quotient is an exact fp16 normal).
+__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t lo4, uint32_t hi4) {
+  return __builtin_bit_cast(v8h, make_uint4(cvt2_e4m3_f16<false>(lo4), cvt2_e4m3_f16<true>(lo4),
+                                            cvt2_e4m3_f16<false>(hi4, 0.0625f), cvt2_e4m3_f16<true>(hi4, 0.0625f)));
+}
+
 // One k-step (128 K) of one wave: 4 MFMAs of K = 32 per weight block and column tile
-// (the first nt of NT tiles), B read from the fp16 LDS chunk.
+// (the first nt of NT tiles). B comes from the E4M3 LDS chunk: per (tile, k-step) two
+// 1 KB halves, half h holding lane (c, g)'s codes 32 g + 16 h .. +16 of token column c
+// (sub-steps 2h and 2h + 1), widened to fp16 in registers.
 template <int NT>
 __device__ __forceinline__ void mma_step(const uint4& a0, const uint4& a1, const uint8_t* lds, int s, int S, int nt,
                                          int lane, uint32_t mlo, uint32_t mhi, v4f* acc0, v4f* acc1) {
-  // tile 0's four B operands are read first (their latency runs under the conversions)
-  v8h b0[4];
+  // tile 0's two halves are read first (their latency runs under the conversions)
+  uint4 b0[2];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
-    b0[m] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(lds + (s * 4 + m) * 1024 + lane * 16));
+  for (int h = 0; h < 2; ++h) b0[h] = *reinterpret_cast<const uint4*>(lds + (s * 2 + h) * 1024 + lane * 16);
 #pragma unroll
   for (int m = 0; m < 4; ++m) {
     const v8h A0 = int4x8_to_f16(word_of(a0, m), mlo, mhi);
     const v8h A1 = int4x8_to_f16(word_of(a1, m), mlo, mhi);
-    acc0[0] = mfma_f16(A0, b0[m], acc0[0]);
-    acc1[0] = mfma_f16(A1, b0[m], acc1[0]);
+    const uint4& bh = b0[m >> 1];
+    const v8h B0 = (m & 1) ? e4m3x8_to_f16(bh.z, bh.w) : e4m3x8_to_f16(bh.x, bh.y);
+    acc0[0] = mfma_f16(A0, B0, acc0[0]);
+    acc1[0] = mfma_f16(A1, B0, acc1[0]);
 #pragma unroll
     for (int j = 1; j < NT; ++j) {
       if (j < nt) {
-        const v8h b = __builtin_bit_cast(
-            v8h, *reinterpret_cast<const uint4*>(lds + ((j * S + s) * 4 + m) * 1024 + lane * 16));
+        const uint2 bj = *reinterpret_cast<const uint2*>(lds + ((j * S + s) * 2 + (m >> 1)) * 1024 + lane * 16 +
+                                                         (m & 1) * 8);
+        const v8h b = e4m3x8_to_f16(bj.x, bj.y);
         acc0[j] = mfma_f16(A0, b, acc0[j]);
         acc1[j] = mfma_f16(A1, b, acc1[j]);
       }
@@ -208,7 +222,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const int nt = min((cnt + 15) >> 4, MAXT);                // column tiles holding rows
   const int k_begin = slice * p.kslice;
   const int k_end = min(p.K, k_begin + p.kslice);
-  const int kc_max = ((p.lds_bytes / (32 * nt)) / (128 * kDepth)) * (128 * kDepth);   // fp16 rows of 16*nt tokens
+  const int kc_max = ((p.lds_bytes / (16 * nt)) / (128 * kDepth)) * (128 * kDepth);   // E4M3 rows of 16*nt tokens
 
   // weight row blocks of this wave: gate|up -> (cb, n_out/16 + cb); down -> (2cb, 2cb + 1)
   const int nthr = blockDim.x;                              // p.waves waves
@@ -262,39 +276,36 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
     const int klen = min(kc_max, k_end - kc0);
     const int S = klen >> 7;                                // k-steps in this chunk
     if (kc0 != k_begin) lds_barrier();                      // LDS reuse
-    // ---- stage the activation rows of this chunk, widened to fp16 once. Unit = 8 codes of
-    //      one row: (tile j, k-step s, sub-step m, lane c + 16 g) -> 16 bytes at
-    //      ((j*S + s)*4 + m)*1024 + lane*16, so MFMA m of k-step s reads one b128 per lane.
+    // ---- stage the activation rows of this chunk as E4M3 bytes. Unit = 16 codes of one
+    //      row: (tile j, k-step s, half h, lane c + 16 g) -> 16 bytes at
+    //      ((j*S + s)*2 + h)*1024 + lane*16, codes 32 g + 16 h .. +16 of the k-step.
     {
       // Threads walk the LDS slots in order (16 bytes each, consecutive threads write
       // consecutive slots: no bank conflicts); slot v of the chunk is
-      // (tile j, k-step st, sub-step m) = v / 64 and lane (c + 16 gg) = v % 64, which holds
-      // codes 8 * (st*16 + gg*4 + m) .. +8 of token column j*16 + c. Batches of kStageBatch
-      // slots per thread issue all their loads (branch-free) before waiting on the first.
-      const int slots = nt * S * 4 * 64;
+      // (tile j, k-step st, half h) = v / 64 and lane (c + 16 gg) = v % 64. Batches of
+      // kStageBatch slots per thread issue all their loads (branch-free) before the first
+      // store.
+      const int slots = nt * S * 2 * 64;
       for (int v0 = 0; v0 < slots; v0 += kStageBatch * nthr) {
-        uint2 q[kStageBatch];
+        uint4 q[kStageBatch];
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
           const int v = v0 + b * nthr + tid;
           const int blk = v >> 6;
-          const int m = blk & 3, js = blk >> 2;
+          const int h = blk & 1, js = blk >> 1;
           const int j = js / S, st = js - j * S;
           uint32_t base = srow[0];
 #pragma unroll
           for (int jj = 1; jj < MAXT; ++jj) base = j == jj ? srow[jj] : base;
-          const uint32_t kk = (uint32_t)(st * 16 + ((tid & 63) >> 4) * 4 + m);
-          const uint32_t off = (v < slots && base != kOutOfRange) ? base + kc0 + kk * 8 : kOutOfRange;
-          q[b] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(ar, off, 0, 0));
+          const uint32_t kk = (uint32_t)(st * 128 + ((tid & 63) >> 4) * 32 + h * 16);
+          const uint32_t off = (v < slots && base != kOutOfRange) ? base + kc0 + kk : kOutOfRange;
+          q[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
         }
 #pragma unroll
         for (int b = 0; b < kStageBatch; ++b) {
           const int v = v0 + b * nthr + tid;
           if (v >= slots) break;
-          // codes 4..7 of each 8 face the weights' high nibbles (16 q): staged divided by 16
-          const uint4 w = make_uint4(cvt2_e4m3_f16<false>(q[b].x), cvt2_e4m3_f16<true>(q[b].x),
-                                     cvt2_e4m3_f16<false>(q[b].y, 0.0625f), cvt2_e4m3_f16<true>(q[b].y, 0.0625f));
-          *reinterpret_cast<uint4*>(lds + (size_t)v * 16) = w;
+          *reinterpret_cast<uint4*>(lds + (size_t)v * 16) = q[b];
         }
       }
     }
@@ -396,12 +407,27 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
       }
     }
   } else {
-    // split K: one LDS chunk (fp16) per slice when an expert holds up to 16 rows; more,
-    // shorter slices (to fill the last round) measured slower: more partial sums to add
+    // split K: slices of at most one E4M3 LDS chunk for 16 rows (4096 K), balanced and
+    // whole rounds of k-steps; more slices only when they fill the last round of
+    // workgroup slots clearly better (each slice adds a partial sum to the combine)
     p.waves = kDecodeWaves;
     p.groups = (p.n_out + 32 * kDecodeWaves - 1) / (32 * kDecodeWaves);
-    p.kslice = std::min(p.K, kDecodeLds / 32);
-    p.ksplit = (p.K + p.kslice - 1) / p.kslice;
+    const int step = 128 * kDepth;
+    const int kmax = std::max(step, (kDecodeLds / 16) / step * step);
+    const long experts = std::min(p.E, 2 * T);
+    const long slots = 2L * device_cus();
+    const int first = (p.K + kmax - 1) / kmax;
+    double best = -1.0;
+    for (int ks = first; ks <= 4 * first; ++ks) {
+      const int kslice = ((p.K + ks - 1) / ks + step - 1) / step * step;
+      if ((p.K + kslice - 1) / kslice != ks) continue;      // rounding merged two slices
+      const double fill = round_fill((long)p.groups * ks * experts, slots);
+      if (fill > best + 0.02) {
+        best = fill;
+        p.kslice = kslice;
+        p.ksplit = ks;
+      }
+    }
   }
 }
 
