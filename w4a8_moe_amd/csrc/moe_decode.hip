@@ -389,15 +389,16 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
   p.lds_bytes = kDecodeLds;
   if (gateup) {
     // The whole reduction (the fused epilogue needs it). Waves per workgroup (16 channels
-    // each): 8, or 7 when that fills the last round of workgroup slots (two per CU)
-    // better; a partly empty last round leaves HBM bandwidth unused. Mixtral-shaped
-    // I = 14336 = 7 * 2048: 7 waves give 1024 workgroups instead of 896 for 512 slots.
+    // each): from 8 down to 4, the count that fills the rounds of workgroup slots (two per
+    // CU) best; a partly empty round leaves HBM bandwidth unused. Mixtral-shaped
+    // I = 14336 = 7 * 2048: 7 waves give 1024 workgroups instead of 896 for 512 slots;
+    // one GPU's 8-way share of Grok-1 (I = 4096): 4 waves give 512 instead of 256.
     p.kslice = p.K;
     p.ksplit = 1;
     const long experts = std::min(p.E, 2 * T);              // experts that can hold rows
     const long slots = 2L * device_cus();
     double best = -1.0;
-    for (int w = kDecodeWaves; w >= std::min(7, kDecodeWaves); --w) {
+    for (int w = kDecodeWaves; w >= std::min(4, kDecodeWaves); --w) {
       const int groups = (p.n_out + 16 * w - 1) / (16 * w);
       const double fill = round_fill((long)groups * experts, slots);
       if (fill > best + 1e-9) {
@@ -408,10 +409,9 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     }
   } else {
     // split K: slices of at most one E4M3 LDS chunk for 16 rows (4096 K), balanced and
-    // whole rounds of k-steps; more slices only when they fill the last round of
-    // workgroup slots clearly better (each slice adds a partial sum to the combine)
-    p.waves = kDecodeWaves;
-    p.groups = (p.n_out + 32 * kDecodeWaves - 1) / (32 * kDecodeWaves);
+    // whole rounds of k-steps, and 4..8 waves per workgroup (32 channels each): the
+    // combination that fills the rounds of workgroup slots best, preferring fewer slices
+    // (each adds a partial sum to the combine) and then more waves (more loads in flight)
     const int step = 128 * kDepth;
     const int kmax = std::max(step, (kDecodeLds / 16) / step * step);
     const long experts = std::min(p.E, 2 * T);
@@ -421,11 +421,16 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     for (int ks = first; ks <= 4 * first; ++ks) {
       const int kslice = ((p.K + ks - 1) / ks + step - 1) / step * step;
       if ((p.K + kslice - 1) / kslice != ks) continue;      // rounding merged two slices
-      const double fill = round_fill((long)p.groups * ks * experts, slots);
-      if (fill > best + 0.02) {
-        best = fill;
-        p.kslice = kslice;
-        p.ksplit = ks;
+      for (int w = kDecodeWaves; w >= std::min(4, kDecodeWaves); --w) {
+        const int groups = (p.n_out + 32 * w - 1) / (32 * w);
+        const double fill = round_fill((long)groups * ks * experts, slots);
+        if (fill > best + 0.02) {
+          best = fill;
+          p.kslice = kslice;
+          p.ksplit = ks;
+          p.waves = w;
+          p.groups = groups;
+        }
       }
     }
   }
