@@ -67,7 +67,7 @@ __device__ __forceinline__ v8i operand_from(uint4 lo, uint4 hi) {
 //   ACT 1, gelu_erf:  g * Phi(g), Phi from erfc(|g|/sqrt 2) = t 2^(Q(t) - g^2 log2(e) / 2),
 //                     t = 1 / (1 + |g| / (2 sqrt 2)), Q a degree-9 polynomial fitted here
 //                     (least squares in Chebyshev form on |g| in [0, 17], max error 8e-8
-//                     in log2 units); Phi = 1 - erfc/2 for g >= 0, erfc/2 below
+//                     in log2 units); g Phi(g) = max(g, 0) - |g| erfc/2 for either sign
 //   ACT 2, gelu_tanh: g/2 (1 + tanh(y)) = g * sigma(2 y), y = sqrt(2/pi) (g + 0.044715 g^3)
 __device__ __forceinline__ float sigmoid_fast(float y) {
   return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-y * 1.4426950408889634f));
@@ -80,20 +80,23 @@ __device__ __forceinline__ float act_fast(float g) {
     const float y = 0.7978845608028654f * __builtin_fmaf(0.044715f * g * g, g, g);
     return g * sigmoid_fast(2.0f * y);
   }
+  // th = t / 2 (the 1/2 of erfc/2 taken into the reciprocal, exactly); Q evaluated in th
+  // with the coefficients of t^k scaled by 2^k, which gives the same fp32 values
   const float a = __builtin_fabsf(g);
-  const float t = __builtin_amdgcn_rcpf(__builtin_fmaf(a, 0.35355339059327373f, 1.0f));
-  float q = 0.22225850820541382f;
-  q = __builtin_fmaf(q, t, -1.0541905164718628f);
-  q = __builtin_fmaf(q, t, 1.8387916088104248f);
-  q = __builtin_fmaf(q, t, -1.2315798997879028f);
-  q = __builtin_fmaf(q, t, 0.07272530347108841f);
-  q = __builtin_fmaf(q, t, -0.0986909419298172f);
-  q = __builtin_fmaf(q, t, 0.08420290797948837f);
-  q = __builtin_fmaf(q, t, 0.5506213307380676f);
-  q = __builtin_fmaf(q, t, 1.4415581226348877f);
-  q = __builtin_fmaf(q, t, -1.8256964683532715f);
-  const float half_erfc = 0.5f * t * __builtin_amdgcn_exp2f(__builtin_fmaf(-g * g, 0.7213475204444817f, q));
-  return g * (g >= 0.0f ? 1.0f - half_erfc : half_erfc);
+  const float th = __builtin_amdgcn_rcpf(__builtin_fmaf(a, 0.70710678118654746f, 2.0f));
+  float q = 113.79635620117188f;
+  q = __builtin_fmaf(q, th, -269.8727722167969f);
+  q = __builtin_fmaf(q, th, 235.36532592773438f);
+  q = __builtin_fmaf(q, th, -78.82111358642578f);
+  q = __builtin_fmaf(q, th, 2.327209711074829f);
+  q = __builtin_fmaf(q, th, -1.5790550708770752f);
+  q = __builtin_fmaf(q, th, 0.673623263835907f);
+  q = __builtin_fmaf(q, th, 2.2024853229522705f);
+  q = __builtin_fmaf(q, th, 2.8831162452697754f);
+  q = __builtin_fmaf(q, th, -1.8256964683532715f);
+  const float half_erfc = th * __builtin_amdgcn_exp2f(__builtin_fmaf(-g * g, 0.7213475204444817f, q));
+  // g * Phi(g) = max(g, 0) - |g| erfc(|g| / sqrt 2) / 2 for either sign
+  return __builtin_fmaf(-a, half_erfc, __builtin_fmaxf(g, 0.0f));
 }
 
 __device__ __forceinline__ float act_fast_rt(float g, int act) {

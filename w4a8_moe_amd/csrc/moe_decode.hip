@@ -59,7 +59,7 @@ namespace w4a8 {
 #endif
 constexpr int kDepth = W4A8_DECODE_DEPTH;
 constexpr int kBody = W4A8_DECODE_BODY;                    // k-steps per unrolled loop body
-constexpr int kStageBatch = 8;                             // staging units in flight per thread
+constexpr int kWaitVmcnt0 = 0x0F70;                        // s_waitcnt vmcnt(0) (expcnt, lgkmcnt: no wait)
 static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
 // an LDS chunk holds at least one round of k-steps for the most column tiles (else the
 // chunk loop could not advance)
@@ -280,34 +280,23 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
     //      row: (tile j, k-step s, half h, lane c + 16 g) -> 16 bytes at
     //      ((j*S + s)*2 + h)*1024 + lane*16, codes 32 g + 16 h .. +16 of the k-step.
     {
-      // Threads walk the LDS slots in order (16 bytes each, consecutive threads write
-      // consecutive slots: no bank conflicts); slot v of the chunk is
-      // (tile j, k-step st, half h) = v / 64 and lane (c + 16 gg) = v % 64. Batches of
-      // kStageBatch slots per thread issue all their loads (branch-free) before the first
-      // store.
-      const int slots = nt * S * 2 * 64;
-      for (int v0 = 0; v0 < slots; v0 += kStageBatch * nthr) {
-        uint4 q[kStageBatch];
+      // Buffer loads straight into LDS (no registers, so all of a wave's units are in
+      // flight at once): one instruction moves a 64-unit block (tile j, k-step st, half h)
+      // = v / 64, lane (c + 16 gg) to v * 16. Lanes of a column past the expert's rows
+      // load out of range, which writes zeros.
+      const int blocks = nt * S * 2;
+      for (int blk = wave; blk < blocks; blk += nthr / kWave) {
+        const int h = blk & 1, js = blk >> 1;
+        const int j = js / S, st = js - j * S;
+        uint32_t base = srow[0];
 #pragma unroll
-        for (int b = 0; b < kStageBatch; ++b) {
-          const int v = v0 + b * nthr + tid;
-          const int blk = v >> 6;
-          const int h = blk & 1, js = blk >> 1;
-          const int j = js / S, st = js - j * S;
-          uint32_t base = srow[0];
-#pragma unroll
-          for (int jj = 1; jj < MAXT; ++jj) base = j == jj ? srow[jj] : base;
-          const uint32_t kk = (uint32_t)(st * 128 + ((tid & 63) >> 4) * 32 + h * 16);
-          const uint32_t off = (v < slots && base != kOutOfRange) ? base + kc0 + kk : kOutOfRange;
-          q[b] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
-        }
-#pragma unroll
-        for (int b = 0; b < kStageBatch; ++b) {
-          const int v = v0 + b * nthr + tid;
-          if (v >= slots) break;
-          *reinterpret_cast<uint4*>(lds + (size_t)v * 16) = q[b];
-        }
+        for (int jj = 1; jj < MAXT; ++jj) base = j == jj ? srow[jj] : base;
+        const uint32_t kk = (uint32_t)(st * 128 + (lane >> 4) * 32 + h * 16);
+        const uint32_t off = base != kOutOfRange ? base + kc0 + kk : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
+                                                 off, 0, 0, 0);
       }
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);            // this wave's LDS loads (vmcnt, not lgkmcnt)
     }
     lds_barrier();
     // ---- stream the weights of this chunk
@@ -389,16 +378,18 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
   p.lds_bytes = kDecodeLds;
   if (gateup) {
     // The whole reduction (the fused epilogue needs it). Waves per workgroup (16 channels
-    // each): from 8 down to 4, the count that fills the rounds of workgroup slots (two per
-    // CU) best; a partly empty round leaves HBM bandwidth unused. Mixtral-shaped
-    // I = 14336 = 7 * 2048: 7 waves give 1024 workgroups instead of 896 for 512 slots;
-    // one GPU's 8-way share of Grok-1 (I = 4096): 4 waves give 512 instead of 256.
+    // each): 8, 7 or 4, the count that fills the rounds of workgroup slots (two per CU)
+    // best; a partly empty round leaves HBM bandwidth unused. Mixtral-shaped I = 14336 =
+    // 7 * 2048: 7 waves give 1024 workgroups instead of 896 for 512 slots; one GPU's
+    // 8-way share of Grok-1 (I = 4096): 4 waves give 512 instead of 256. (5 and 6 waves
+    // measured 15-40% slower than these at both shapes, 7 slow at the second.)
     p.kslice = p.K;
     p.ksplit = 1;
     const long experts = std::min(p.E, 2 * T);              // experts that can hold rows
     const long slots = 2L * device_cus();
     double best = -1.0;
-    for (int w = kDecodeWaves; w >= std::min(4, kDecodeWaves); --w) {
+    for (int w : {8, 7, 4}) {
+      if (w > kDecodeWaves) continue;
       const int groups = (p.n_out + 16 * w - 1) / (16 * w);
       const double fill = round_fill((long)groups * experts, slots);
       if (fill > best + 1e-9) {
@@ -408,12 +399,13 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
       }
     }
   } else {
-    // split K: slices of at most one E4M3 LDS chunk for 16 rows (4096 K), balanced and
-    // whole rounds of k-steps, and 4..8 waves per workgroup (32 channels each): the
-    // combination that fills the rounds of workgroup slots best, preferring fewer slices
-    // (each adds a partial sum to the combine) and then more waves (more loads in flight)
-    const int step = 128 * kDepth;
-    const int kmax = std::max(step, (kDecodeLds / 16) / step * step);
+    // split K: slices of at most one E4M3 LDS chunk for 16 rows (4096 K), balanced to whole
+    // k-steps (a chunk may end with a partial round), and 4..8 waves per workgroup (32
+    // channels each): the combination that fills the rounds of workgroup slots best,
+    // preferring fewer slices (each adds a partial sum to the combine) and then more waves
+    // (more loads in flight)
+    const int step = 128;
+    const int kmax = (kDecodeLds / 16) / (128 * kDepth) * (128 * kDepth);
     const long experts = std::min(p.E, 2 * T);
     const long slots = 2L * device_cus();
     const int first = (p.K + kmax - 1) / kmax;
