@@ -24,6 +24,9 @@ Each function names the passage of the source pages it follows:
   (FreeToken pull request 392): block-FP8 (FP8_PB_WO) weight-only projections with
   per-128x128-block scales ``weight_scale_inv``, shapes [16384,2560] with scales
   [128,20] and [13312,2560] with scales [104,20].
+* the per-tensor FP8 dense linear (``fp8_linear``) follows page A's ``quant_method``
+  "fp8" with static activations (everything but the router gates and ``lm_head``) and
+  page B's tensor-wise FP8 quantization.
 
 Where the pages leave a step open, the reading taken is stated at the function.
 Parity pins for every function live in ``tests/test_oracle_*.py``.
@@ -37,6 +40,7 @@ from .moe import (ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH, activation, act_lipschi
                   expert_gate_up, expert_down,
                   moe_error_bound)
 from .block_fp8 import fp8_block_quantize, fp8_block_linear, fp8_block_linear_bruteforce
+from .fp8_linear import fp8_tensor_quantize, fp8_quantize_activations, fp8_linear, fp8_linear_bruteforce
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_table",
@@ -47,4 +51,5 @@ __all__ = [
     "quantize_static", "static_scale", "moe_forward", "moe_reference_unquantized",
     "moe_error_bound", "expert_gate_up", "expert_down",
     "fp8_block_quantize", "fp8_block_linear", "fp8_block_linear_bruteforce",
+    "fp8_tensor_quantize", "fp8_quantize_activations", "fp8_linear", "fp8_linear_bruteforce",
 ]

@@ -5,7 +5,8 @@ The pages fix that activation scales are static (page "ROCm: enable trillion-par
 MoE models with INT4-FP8 single node", quantization_config: activation_scheme static)
 but print no values. Reading: s_x = fp32(max|x| / 448) over the layer's input and
 s_a = fp32(max|a| / 448) over the gated intermediate of an oracle pass (for the prefill
-workload: over the oracle's sampled token subset). Calls only oracle/ and synth/.
+workload: over the oracle's sampled token subset); for the per-tensor FP8 dense linear
+workloads, s_x = fp32(max|x| / 448) over their rows. Calls only oracle/ and synth/.
 
     python tests/golden/make_static_scales.py [config ...]
 """
@@ -56,13 +57,24 @@ def calibrate(cfg):
             "s_a_hex": float(s_a).hex(), "calibration_tokens": "all" if tokens is None else int(tokens.size)}
 
 
+def calibrate_linear(cfg):
+    """Per-tensor FP8 dense linear: the static activation scale over the workload's rows."""
+    x = synth.block_activations(cfg)
+    s_x = oracle.static_scale(np.max(np.abs(oracle.bf16_to_f32(x))))
+    print(f"{cfg.name}: s_x={float(s_x)!r}", flush=True)
+    return {"s_x": float(s_x), "s_x_hex": float(s_x).hex(), "calibration_tokens": "all"}
+
+
 def main(names):
     data = json.load(open(OUT)) if os.path.exists(OUT) else {}
     data["_written_by"] = "tests/golden/make_static_scales.py (oracle calibration pass)"
     for name in names:
-        data[name] = calibrate(synth.MOE_CONFIGS[name])
+        if name in synth.LINEAR_CONFIGS:
+            data[name] = calibrate_linear(synth.LINEAR_CONFIGS[name])
+        else:
+            data[name] = calibrate(synth.MOE_CONFIGS[name])
         json.dump(data, open(OUT, "w"), indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":
-    main(sys.argv[1:] or list(synth.MOE_CONFIGS))
+    main(sys.argv[1:] or list(synth.MOE_CONFIGS) + list(synth.LINEAR_CONFIGS))
