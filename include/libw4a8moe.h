@@ -5,8 +5,8 @@
  * The method, as the source pages state it:
  *  - page "ROCm: enable trillion-parameter MoE models with INT4-FP8 single node"
  *    (sglang pull request 4152): "INT4 MoE weights, FP8 compute"; the Grok-1
- *    W4A8KV8 config.json quantization_config: int4_experts {bits 4, sym true,
- *    group column}, activation_scheme static, export pack_method reorder; routing
+ *    W4A8KV8 config.json quantization_config: quant_method fp8, int4_experts {bits 4,
+ *    sym true, group column}, activation_scheme static, export pack_method reorder; routing
  *    num_local_experts 8, num_experts_per_tok 2, the router gate left unquantized
  *    (ignored_layers).
  *  - page "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm" (sglang
@@ -77,6 +77,8 @@ extern "C" {
 #define W4A8_OP_GEMM1_BF16    3   /* gemm1 with a bf16 x (holds the quantized x) */
 #define W4A8_OP_GEMM2         4   /* args: T, H, I, E */
 #define W4A8_OP_BLOCK_LINEAR  5   /* args: M, N, K, - */
+#define W4A8_OP_TENSOR_QUANT  6   /* args: -, -, -, - */
+#define W4A8_OP_FP8_LINEAR    7   /* args: M, N, K, - */
 
 /* Size limits checked by every MoE call. */
 #define W4A8_MAX_EXPERTS 256
@@ -244,6 +246,37 @@ int32_t fp8_block_quant(const uint16_t* w_bf16, int32_t N, int32_t K,
 int32_t fp8_block_linear(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float* s,
                          int32_t M, int32_t N, int32_t K, uint16_t* y_bf16,
                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8_tensor_quant -- tensor-wise FP8 quantization of a dense bf16 weight (page "ROCm:
+ *   enable trillion-parameter MoE models with INT4-FP8 single node": quant_method "fp8"
+ *   for every linear but the router gates and lm_head; page "[AMD][Quantization] Add
+ *   int4fp8_moe online quantization on ROCm": tensor-wise FP8 quantization):
+ *     s_w = fp32(max|w| / 448) (correctly rounded), w_e4m3 = e4m3(fp32(w / s_w)) (nearest
+ *     even, saturating); an all-zero tensor gives s_w = 0 and zero codes.
+ *   w_bf16 [n] (n >= 1), w_e4m3 [n] (out), s_w (out, one float in device memory; it is
+ *   written by the second of the call's two launches). Deterministic.
+ *   Workspace: w4a8_workspace_bytes(W4A8_OP_TENSOR_QUANT, 0, 0, 0, 0) bytes (partial maxima).
+ *   Non-finite weights give undefined output.
+ */
+int32_t fp8_tensor_quant(const uint16_t* w_bf16, int64_t n, uint8_t* w_e4m3, float* s_w,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8_linear_w8a8 -- per-tensor static FP8 dense linear for decode rows (the same two
+ *   pages; activation_scheme static):
+ *   xq = e4m3(fp32(x / s_x)) (as fp8_quant_static, into the workspace), then
+ *   y[m][n] = bf16( fp32(s_x * s_w) * sum_k dec(xq[m][k]) * dec(w[n][k]) ), nearest even;
+ *   the products are exact and summed in fp32.
+ *   x_bf16 [M][K], s_x > 0 (static activation scale, host value), w_e4m3 [N][K] with its
+ *   tensor scale s_w >= 0 (host value), y_bf16 [M][N] (out).
+ *   Requires 1 <= M <= 16, N % 16 == 0, K % 128 == 0; M * K <= 65536 (the codes of x are
+ *   staged in LDS; W4A8_ERR_UNSUPPORTED above).
+ *   Workspace: w4a8_workspace_bytes(W4A8_OP_FP8_LINEAR, M, N, K, 0) bytes (holds xq).
+ */
+int32_t fp8_linear_w8a8(const uint16_t* x_bf16, float s_x, const uint8_t* w_e4m3, float s_w,
+                        int32_t M, int32_t N, int32_t K, uint16_t* y_bf16,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /* Workspace size in bytes of one call (0 when none is needed); 0 also for bad args. */
 size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t I_or_K, int32_t E);

@@ -18,8 +18,8 @@ def L():
 def test_exports_every_declared_function(L):
     names = W.header_functions()
     assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_route_sort_quant", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
-                          "fp8_block_quant", "fp8_block_linear", "w4a8_workspace_bytes", "w4a8_status_str",
-                          "w4a8_moe_kernel"}
+                          "fp8_block_quant", "fp8_block_linear", "fp8_tensor_quant", "fp8_linear_w8a8",
+                          "w4a8_workspace_bytes", "w4a8_status_str", "w4a8_moe_kernel"}
     for n in names:
         assert hasattr(L, n), n
 
@@ -164,3 +164,34 @@ def test_block_validation(L):
 def test_workspace_bad_args(L):
     assert W.workspace_bytes(99, 1, 1, 1, 1) == 0
     assert W.workspace_bytes(W.OP_GEMM2, 32, 100, 512, 8) == 0
+
+
+def test_fp8_tensor_quant_validation(L):
+    nws = W.workspace_bytes(W.OP_TENSOR_QUANT, 0, 0, 0, 0)
+    assert nws == 1024 * 4
+    assert L.fp8_tensor_quant(A, 0, A, A, A, nws, None) == W.ERR_SHAPE
+    assert L.fp8_tensor_quant(None, 16, A, A, A, nws, None) == W.ERR_NULL
+    assert L.fp8_tensor_quant(A, 16, A, None, A, nws, None) == W.ERR_NULL
+    assert L.fp8_tensor_quant(A, 16, A, A, None, nws, None) == W.ERR_NULL
+    assert L.fp8_tensor_quant(U, 16, A, A, A, nws, None) == W.ERR_ALIGN
+    assert L.fp8_tensor_quant(A, 16, A, A, A, nws - 1, None) == W.ERR_WORKSPACE
+
+
+def test_fp8_linear_w8a8_validation(L):
+    def call(M=8, N=256, K=512, s_x=0.01, s_w=0.001, x=A, w=A, y=A, ws=A, nws=None):
+        if nws is None:
+            nws = W.workspace_bytes(W.OP_FP8_LINEAR, M, N, K, 0)
+        return L.fp8_linear_w8a8(x, s_x, w, s_w, M, N, K, y, ws, nws, None)
+    assert W.workspace_bytes(W.OP_FP8_LINEAR, 8, 256, 6144, 0) == 8 * 6144
+    assert call(M=0) == W.ERR_SHAPE
+    assert call(M=17) == W.ERR_SHAPE
+    assert call(N=24) == W.ERR_SHAPE                            # N % 16
+    assert call(K=192) == W.ERR_SHAPE                           # K % 128
+    assert call(M=16, K=8192) == W.ERR_UNSUPPORTED              # M * K > 65536
+    assert call(s_x=0.0) == W.ERR_ARG
+    assert call(s_w=-1.0) == W.ERR_ARG
+    assert call(s_w=float("nan")) == W.ERR_ARG
+    assert call(x=None) == W.ERR_NULL
+    assert call(ws=None) == W.ERR_NULL
+    assert call(y=U) == W.ERR_ALIGN
+    assert call(nws=16) == W.ERR_WORKSPACE

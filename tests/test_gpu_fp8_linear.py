@@ -1,0 +1,88 @@
+"""GPU parity of the per-tensor FP8 (W8A8) dense linear and its tensor-wise quantizer
+against the oracle, through the C ABI: codes and scale bit-exact; outputs to the final
+bar (|d| <= 1e-2 max|ref|, <= 0.1% of elements above 1e-3 max|ref|, against the oracle's
+bf16 rounding), bit-exact in the integer case; deterministic."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import w4a8_moe_amd as W
+from tests.gpu_util import assert_final_close, bf16_bits_to_f64, bf16_dev, host, same_codes, static_scales, torch
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("N,K", [(1, 8), (3, 40), (16, 128), (257, 384), (64, 2560 + 8)])
+def test_tensor_quant_bit_exact(N, K):
+    cfg = synth.custom_block("tq", M=1, N=N, K=K, cfg=91, sub=N)
+    w = synth.block_weights(cfg)
+    q, s = W.fp8_tensor_quant(bf16_dev(w))
+    qo, so = oracle.fp8_tensor_quantize(w)
+    assert host(s)[0] == so
+    assert same_codes(host(q), qo).all()
+
+
+def test_tensor_quant_zeros():
+    q, s = W.fp8_tensor_quant(bf16_dev(np.zeros((16, 256), np.uint16)))
+    assert host(s)[0] == 0.0 and not host(q).any()
+
+
+def test_integer_case_bit_exact():
+    """Integer x with s_x = 1 and s_w = 1: every product and partial sum is an integer
+    below 2^24, so the fp32 sums are exact in any order and y equals the oracle's bits."""
+    rng = np.random.default_rng(92)
+    M, N, K = 5, 96, 256
+    xi = rng.integers(-8, 9, size=(M, K)).astype(np.float32)
+    codes = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0
+    x = synth.f32_to_bf16_bits(xi)
+    y = W.fp8_linear_w8a8(bf16_dev(x), 1.0, torch().from_numpy(codes).cuda(), 1.0)
+    _, ybits, _ = oracle.fp8_linear(x, np.float32(1.0), codes, np.float32(1.0))
+    assert np.array_equal(host(y), ybits)
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 256, 384), (8, 400, 256), (16, 128, 4096), (3, 1024, 6144), (10, 48, 6144),
+                                   (2, 16, 128)])
+def test_fp8_linear_parity(M, N, K):
+    cfg = synth.custom_block("fl", M=M, N=N, K=K, cfg=93, sub=N)
+    w = synth.block_weights(cfg)
+    x = synth.block_activations(cfg)
+    s_x = oracle.static_scale(np.max(np.abs(bf16_to_f32(x)))) * np.float32(0.75)    # some codes saturate
+    qo, so = oracle.fp8_tensor_quantize(w)
+    q, s = W.fp8_tensor_quant(bf16_dev(w))
+    assert same_codes(host(q), qo).all() and host(s)[0] == so
+    ws = torch().zeros(W.workspace_bytes(W.OP_FP8_LINEAR, M, N, K, 0), dtype=torch().uint8, device="cuda")
+    y = W.fp8_linear_w8a8(bf16_dev(x), s_x, q, float(so), ws=ws)
+    _, ybits, xq = oracle.fp8_linear(x, s_x, qo, so)
+    assert same_codes(host(ws)[:M * K].reshape(M, K), xq).all()          # the staged activation codes
+    assert_final_close(bf16_bits_to_f64(host(y)), bf16_bits_to_f64(ybits))
+    y2 = W.fp8_linear_w8a8(bf16_dev(x), s_x, q, float(so))
+    assert torch().equal(y, y2)                                          # deterministic
+
+
+def bf16_to_f32(bits):
+    return oracle.bf16_to_f32(bits)
+
+
+@pytest.mark.parametrize("name", sorted(synth.LINEAR_CONFIGS))
+def test_fp8_linear_page_shapes(name):
+    """The Grok-1 attention projections at decode rows 1 and 8, every output."""
+    cfg = synth.LINEAR_CONFIGS[name]
+    s_x = static_scales_linear(name)
+    w = synth.block_weights(cfg)
+    x = synth.block_activations(cfg)
+    q, s = W.fp8_tensor_quant(bf16_dev(w))
+    qo, so = oracle.fp8_tensor_quantize(w)
+    assert host(s)[0] == so and same_codes(host(q), qo).all()
+    y = W.fp8_linear_w8a8(bf16_dev(x), s_x, q, float(host(s)[0]))
+    _, ybits, _ = oracle.fp8_linear(x, s_x, qo, so)
+    assert_final_close(bf16_bits_to_f64(host(y)), bf16_bits_to_f64(ybits))
+
+
+def static_scales_linear(name):
+    import json
+    import os
+    from tests.gpu_util import GOLDEN
+    d = json.load(open(os.path.join(GOLDEN, "static_scales.json")))[name]
+    return np.float32(float.fromhex(d["s_x_hex"]))

@@ -21,6 +21,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_ARG, ERR
 ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
 DT_F32, DT_BF16, DT_E4M3 = 0, 1, 2
 OP_ROUTE_SORT, OP_GEMM1, OP_GEMM1_BF16, OP_GEMM2, OP_BLOCK_LINEAR = 1, 2, 3, 4, 5
+OP_TENSOR_QUANT, OP_FP8_LINEAR = 6, 7
 
 _lock = threading.Lock()
 _lib = None
@@ -42,6 +43,8 @@ _SIGNATURES = {
     "moe_gemm2_w4a8": (_I32, [_P, _F32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "fp8_block_quant": (_I32, [_P, _I32, _I32, _P, _P, _P]),
     "fp8_block_linear": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "fp8_tensor_quant": (_I32, [_P, _I64, _P, _P, _P, _SZ, _P]),
+    "fp8_linear_w8a8": (_I32, [_P, _F32, _P, _F32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "w4a8_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "w4a8_status_str": (ctypes.c_char_p, [_I32]),
     "w4a8_moe_kernel": (_I32, [_I32]),
@@ -302,6 +305,37 @@ def fp8_block_linear(x, w, s, out=None):
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     _check("fp8_block_linear", lib().fp8_block_linear(_ptr(x), _ptr(w), _ptr(s), M, N, K, _ptr(y), None, 0,
                                                       _stream(x.device)))
+    return y
+
+
+def fp8_tensor_quant(w):
+    """bf16 weight (any shape) -> (uint8 E4M3 codes of the same shape, fp32 scale [1] on the
+    device): one scale fp32(max|w| / 448) for the tensor."""
+    torch = _torch()
+    _need(w, torch.bfloat16, tuple(w.shape), "w")
+    q = torch.empty(tuple(w.shape), dtype=torch.uint8, device=w.device)
+    s = torch.empty(4, dtype=torch.float32, device=w.device)         # 16 bytes: the scale in [0]
+    nws = workspace_bytes(OP_TENSOR_QUANT, 0, 0, 0, 0)
+    ws = _workspace(nws, w.device)
+    _check("fp8_tensor_quant", lib().fp8_tensor_quant(_ptr(w), w.numel(), _ptr(q), _ptr(s), _ptr(ws), ws.numel(),
+                                                      _stream(w.device)))
+    return q, s[:1]
+
+
+def fp8_linear_w8a8(x, s_x, w, s_w, out=None, ws=None):
+    """bf16 x [M, K] with its static scale s_x, E4M3 w [N, K] with its tensor scale s_w
+    (host floats) -> bf16 y [M, N]."""
+    torch = _torch()
+    M, K = x.shape
+    N = w.shape[0]
+    _need(x, torch.bfloat16, (M, K), "x")
+    _need(w, torch.uint8, (N, K), "w")
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
+    nws = workspace_bytes(OP_FP8_LINEAR, M, N, K, 0)
+    if ws is None or ws.numel() < nws:
+        ws = _workspace(nws, x.device)
+    _check("fp8_linear_w8a8", lib().fp8_linear_w8a8(_ptr(x), float(s_x), _ptr(w), float(s_w), M, N, K, _ptr(y),
+                                                    _ptr(ws), ws.numel(), _stream(x.device)))
     return y
 
 

@@ -21,6 +21,12 @@
 // Tuning knobs (defaults chosen by measurement on MI355X): W4A8_BL_SPLIT waves per row
 // block, W4A8_BL_DEPTH blocks in flight, W4A8_BL_RB_SMALL_M / W4A8_BL_RB_LARGE_M row
 // blocks per workgroup for M <= 2 / M > 2.
+//
+// The per-tensor FP8 linear (fp8_linear_kernel, the dense projections of the W4A8 model:
+// quant_method "fp8" with static activations on the page "ROCm: enable trillion-parameter
+// MoE models with INT4-FP8 single node") has the same mapping; its activations arrive as
+// E4M3 codes and are staged as bytes (M x K in LDS, half the bf16 size), both operands are
+// widened to bf16 in registers (exact), and the one scale s_x * s_w multiplies the sum.
 #include <algorithm>
 
 #include "common.h"
@@ -159,6 +165,105 @@ void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s
   // fewer row blocks per workgroup while staging x costs little, more as M grows
   if (M <= 2) launch_bl<W4A8_BL_RB_SMALL_M>(x, w, s, M, N, K, y, st);
   else launch_bl<W4A8_BL_RB_LARGE_M>(x, w, s, M, N, K, y, st);
+}
+
+// ---------------------------------------------------------------- per-tensor FP8 linear
+// y[m][n] = bf16( scale * sum_k dec(xq[m][k]) * dec(W[n][k]) ), scale = s_x * s_w.
+// Staged unit (kb, j, g, m) = 8 codes of x[m][kb*128 + g*32 + j*8 .. +8] at byte
+// ((((kb*4 + j)*4 + g)*M + m) << 3): lane (m, g) of MFMA j reads 8 contiguous bytes.
+template <int RB>   // 16-row blocks per workgroup
+__global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
+    uint16_t* __restrict__ y) {
+  constexpr int kWaves = RB * kBlSplit;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int KB = K >> 7;
+  const int units = M * (K >> 3);
+  for (int u = tid; u < units; u += kWaves * kWave) {
+    const int m = u / (K >> 3), c8 = u - m * (K >> 3);
+    const int kb = c8 >> 4, within = c8 & 15;
+    const int g = within >> 2, j = within & 3;
+    const uint2 v = *reinterpret_cast<const uint2*>(xq + (size_t)m * K + c8 * 8);
+    *reinterpret_cast<uint2*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 3)) = v;
+  }
+  __syncthreads();
+  const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);
+  const bool rb_ok = blockIdx.x * RB + wave / kBlSplit < N / 16;
+  const int part_k = wave % kBlSplit;
+  const int i = lane & 15, g = lane >> 4;
+  const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
+  const bool col_ok = i < M;
+  const int per = (KB + kBlSplit - 1) / kBlSplit;
+  const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  uint4 q0[kBlDepth], q1[kBlDepth];
+#pragma unroll
+  for (int d = 0; d < kBlDepth; ++d)
+    if (kb_begin + d < kb_end) {
+      q0[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128);
+      q1[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128 + 16);
+    }
+  for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kBlDepth) {
+#pragma unroll
+    for (int d = 0; d < kBlDepth; ++d) {
+      const int kb = kb0 + d;
+      if (kb < kb_end) {
+        const uint4 a0 = q0[d], a1 = q1[d];
+        if (kb + kBlDepth < kb_end) {
+          q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128);
+          q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128 + 16);
+        }
+        const uint32_t c[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {                        // MFMA j: bytes 8j..8j+7 of the lane's 32
+          uint32_t d0, d1, d2, d3;
+          e4m3x4_to_bf16x4(c[2 * j], d0, d1);
+          e4m3x4_to_bf16x4(c[2 * j + 1], d2, d3);
+          const v8bf a = bf16_operand(d0, d1, d2, d3);
+          uint2 bx = make_uint2(0u, 0u);
+          if (col_ok) bx = *reinterpret_cast<const uint2*>(lds + ((((kb * 4 + j) * 4 + g) * M + i) << 3));
+          uint32_t e0, e1, e2, e3;
+          e4m3x4_to_bf16x4(bx.x, e0, e1);
+          e4m3x4_to_bf16x4(bx.y, e2, e3);
+          acc = mfma_bf16_16x16x32(a, bf16_operand(e0, e1, e2, e3), acc);
+        }
+      }
+    }
+  }
+  // the partial sums of a row block's waves meet in LDS (over the staged codes, once every
+  // wave is done with them): its K-part 0 wave adds parts 1, 2, 3 in order
+  v4f* part = reinterpret_cast<v4f*>(lds);
+  __syncthreads();
+  if (part_k > 0) part[(wave - 1) * kWave + lane] = acc;
+  __syncthreads();
+  if (part_k > 0 || !col_ok || !rb_ok) return;
+#pragma unroll
+  for (int v = 1; v < kBlSplit; ++v) {
+    const v4f o = part[(wave + v - 1) * kWave + lane];
+    acc[0] += o[0]; acc[1] += o[1]; acc[2] += o[2]; acc[3] += o[3];
+  }
+  const int n = rb * 16 + 4 * g;
+  uint2 o;
+  o.x = f32_to_bf16_bits(scale * acc[0]) | f32_to_bf16_bits(scale * acc[1]) << 16;
+  o.y = f32_to_bf16_bits(scale * acc[2]) | f32_to_bf16_bits(scale * acc[3]) << 16;
+  *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
+}
+
+template <int RB>
+static void launch_fl(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
+                      hipStream_t st) {
+  const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
+  const size_t lds = std::max((size_t)M * K, (size_t)(RB * kBlSplit - 1) * kWave * sizeof(v4f));
+  hipLaunchKernelGGL(fp8_linear_kernel<RB>, dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w, scale, M, N,
+                     K, y);
+}
+
+void launch_fp8_linear(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
+                       hipStream_t st) {
+  if (M <= 2) launch_fl<W4A8_BL_RB_SMALL_M>(xq, w, scale, M, N, K, y, st);
+  else launch_fl<W4A8_BL_RB_LARGE_M>(xq, w, scale, M, N, K, y, st);
 }
 
 }  // namespace w4a8

@@ -20,6 +20,10 @@ void launch_w4_tile(const int32_t* packed, int64_t E, int N, int K, int32_t* til
 void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st);
 int fp8_quant_blocks(int64_t n);      // 256-thread workgroups of one quantization launch
 void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st);
+constexpr int kTensorQuantParts = 1024;   // most partial maxima of one fp8_tensor_quant
+// two launches: partial maxima into partial[kTensorQuantParts], then scale + codes
+void launch_fp8_tensor_quant(const uint16_t* w, int64_t n, uint8_t* q, float* s, uint32_t* partial,
+                             hipStream_t st);
 
 // ---- route.hip
 size_t route_workspace_bytes(int T, int E);
@@ -79,5 +83,8 @@ void launch_combine(const float* partial, int ksplit, int P, int H, const int32_
 // ---- block_linear.hip
 void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K,
                              uint16_t* y, hipStream_t st);
+// per-tensor FP8 linear on E4M3 activation codes: y = bf16(scale * sum_k xq * wq)
+void launch_fp8_linear(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
+                       hipStream_t st);
 
 }  // namespace w4a8

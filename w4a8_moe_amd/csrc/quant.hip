@@ -8,6 +8,9 @@
 //    activation_scheme static).
 //  * fp8_block_quant: 128x128 block-scaled E4M3 weights (FP8_PB_WO layout of the page
 //    "qwen4_exp: serve the block-FP8 dense projections natively (+25% decode)").
+//  * fp8_tensor_quant: tensor-wise E4M3 weights, one scale max|w| / 448 for the tensor
+//    (the dense projections of the first page's quant_method "fp8"; tensor-wise FP8
+//    quantization in the Highlights of the second).
 // All quotients are formed with the correctly rounded fp32 division (the library is
 // built without fast-math), then rounded to nearest even.
 #include <algorithm>
@@ -153,6 +156,72 @@ __global__ __launch_bounds__(256) void fp8_block_quant_kernel(const uint16_t* __
 void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st) {
   dim3 grid((K + 127) / 128, (N + 127) / 128);
   hipLaunchKernelGGL(fp8_block_quant_kernel, grid, dim3(256), 0, st, w, N, K, q, S);
+}
+
+// ---------------------------------------------------------------- fp8_tensor_quant
+// Pass 1: each workgroup reduces max|w| over a grid-stride share of the tensor (bf16
+// magnitudes compare as integers) into partial[block]. Pass 2: every workgroup reduces
+// the partial maxima (order-independent, so deterministic), forms s = fp32(amax / 448)
+// and quantizes its share with fp8_quant_span; workgroup 0 stores s. amax = 0 gives s = 0
+// and all-zero codes.
+constexpr int kTqThreads = 256;
+
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v) {
+  __shared__ uint32_t red[kTqThreads / kWave];
+#pragma unroll
+  for (int o = kWave / 2; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  if (lane_id() == 0) red[wave_id()] = v;
+  __syncthreads();
+  uint32_t r = 0;
+#pragma unroll
+  for (int w = 0; w < kTqThreads / kWave; ++w) r = max(r, red[w]);
+  return r;
+}
+
+__global__ __launch_bounds__(kTqThreads) void tensor_amax_kernel(const uint16_t* __restrict__ w, int64_t n,
+                                                                 uint32_t* __restrict__ partial) {
+  const int64_t first = blockIdx.x * (int64_t)kTqThreads + threadIdx.x, stride = (int64_t)gridDim.x * kTqThreads;
+  const uint4* src = reinterpret_cast<const uint4*>(w);
+  uint32_t m = 0;
+  for (int64_t i = first; i < (n >> 3); i += stride) {
+    const uint4 v = src[i];
+    m = max(m, max(max(v.x & 0x7FFFu, v.x >> 16 & 0x7FFFu), max(v.y & 0x7FFFu, v.y >> 16 & 0x7FFFu)));
+    m = max(m, max(max(v.z & 0x7FFFu, v.z >> 16 & 0x7FFFu), max(v.w & 0x7FFFu, v.w >> 16 & 0x7FFFu)));
+  }
+  const int64_t t = (n >> 3) * 8 + first;                   // the n % 8 tail
+  if (t < n && first < 8) m = max(m, (uint32_t)w[t] & 0x7FFFu);
+  m = block_max_u32(m);
+  if (threadIdx.x == 0) partial[blockIdx.x] = m;
+}
+
+__global__ __launch_bounds__(kTqThreads) void tensor_quant_kernel(const uint16_t* __restrict__ w, int64_t n,
+                                                                  const uint32_t* __restrict__ partial, int parts,
+                                                                  uint8_t* __restrict__ q, float* __restrict__ s_out) {
+  uint32_t m = 0;
+  for (int i = threadIdx.x; i < parts; i += kTqThreads) m = max(m, partial[i]);
+  m = block_max_u32(m);
+  const float s = bf16_bits_to_f32(m) / 448.0f;             // correctly rounded
+  if (blockIdx.x == 0 && threadIdx.x == 0) *s_out = s;
+  const int64_t first = blockIdx.x * (int64_t)kTqThreads + threadIdx.x, stride = (int64_t)gridDim.x * kTqThreads;
+  if (s > 0.0f) {
+    fp8_quant_span(w, n, s, q, first, stride);
+  } else {
+    for (int64_t i = first; i < (n >> 3); i += stride) reinterpret_cast<uint2*>(q)[i] = make_uint2(0u, 0u);
+    const int64_t t = (n >> 3) * 8 + first;
+    if (t < n && first < 8) q[t] = 0;
+  }
+}
+
+int tensor_quant_parts(int64_t n) {
+  return (int)std::min<int64_t>(std::max<int64_t>(((n >> 3) + kTqThreads - 1) / kTqThreads, 1), kTensorQuantParts);
+}
+
+void launch_fp8_tensor_quant(const uint16_t* w, int64_t n, uint8_t* q, float* s, uint32_t* partial,
+                             hipStream_t st) {
+  const int parts = tensor_quant_parts(n);
+  hipLaunchKernelGGL(tensor_amax_kernel, dim3((unsigned)parts), dim3(kTqThreads), 0, st, w, n, partial);
+  hipLaunchKernelGGL(tensor_quant_kernel, dim3((unsigned)parts), dim3(kTqThreads), 0, st, w, n, partial, parts, q,
+                     s);
 }
 
 }  // namespace w4a8
