@@ -8,8 +8,8 @@ moe_gemm2_w4a8 (down + combine); four consecutive steps are captured in one HIP 
 as a model's decode graph holds its consecutive layers, and exactly K steps are timed. Inputs
 (packed weights, scales, x, logits) are resident in HBM before the timed region. The
 packed weights are rotated over several copies when one copy would fit in the 256 MB
-Infinity Cache, so that the HBM stream is measured. w4_pack + w4_tile (load time) and the block-FP8
-GEMV are timed separately and reported in the same JSON line.
+Infinity Cache, so that the HBM stream is measured. w4_pack + w4_tile (load time), the block-FP8
+GEMV and the per-tensor FP8 (W8A8) linear are timed separately and reported in the same JSON line.
 
 Prints one JSON line.
 """
@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_decode", choices=sorted(synth.MOE_CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-block-gemv", action="store_true", help="skip timing the block-FP8 GEMVs")
+    ap.add_argument("--no-block-gemv", action="store_true",
+                    help="skip timing the block-FP8 GEMVs and the per-tensor FP8 linears")
     ap.add_argument("--no-prefill", action="store_true",
                     help="with the default decode workload, skip the prefill layer's line")
     ap.add_argument("--copy-ref", action="store_true",
@@ -152,6 +153,38 @@ def bench_block_gemv(torch, W, dev, reps=16, iters=50):
         torch.cuda.synchronize()
         us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
         nbytes = cfg.N * cfg.K + S.numel() * 4 + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2
+        out[cfg.name] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
+                         "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+        del qs
+    return out
+
+
+def bench_fp8_linear(torch, W, dev, reps=16, iters=50):
+    """Per-tensor FP8 (W8A8) linear at the Grok-1 attention projection shapes: the call
+    (x quantized to E4M3 and the GEMV, one launch) timed on the library's stream; weights rotated over
+    `reps` copies (>= 590 MB, past the Infinity Cache)."""
+    out = {}
+    d = json.load(open(os.path.join(ROOT, "tests", "golden", "static_scales.json")))
+    for cfg in synth.LINEAR_CONFIGS.values():
+        s_x = float.fromhex(d[cfg.name]["s_x_hex"])
+        w = bf16_dev(torch, synth.block_weights(cfg), dev)
+        q, s = W.fp8_tensor_quant(w)
+        s_w = float(s.item())
+        del w
+        qs = [q.clone() for _ in range(reps)]
+        x = bf16_dev(torch, synth.block_activations(cfg), dev)
+        y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
+        for i in range(5):
+            W.fp8_linear_w8a8(x, s_x, qs[i % reps], s_w, out=y)
+        st = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(st)
+        for i in range(iters):
+            W.fp8_linear_w8a8(x, s_x, qs[i % reps], s_w, out=y)
+        ev[1].record(st)
+        torch.cuda.synchronize()
+        us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+        nbytes = cfg.N * cfg.K + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2     # weights, bf16 x in, bf16 y out
         out[cfg.name] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
         del qs
@@ -340,6 +373,7 @@ def main():
         result["copy_ref_bytes"] = 1 << 30
     if not args.no_block_gemv:
         result["block_fp8_gemv"] = bench_block_gemv(torch, W, dev)
+        result["fp8_linear_w8a8"] = bench_fp8_linear(torch, W, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, *static_scales(cfg.name), ids)
     print(json.dumps(result), flush=True)

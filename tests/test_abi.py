@@ -183,6 +183,10 @@ def test_fp8_linear_w8a8_validation(L):
             nws = W.workspace_bytes(W.OP_FP8_LINEAR, M, N, K, 0)
         return L.fp8_linear_w8a8(x, s_x, w, s_w, M, N, K, y, ws, nws, None)
     assert W.workspace_bytes(W.OP_FP8_LINEAR, 8, 256, 6144, 0) == 8 * 6144
+    assert W.workspace_bytes(W.OP_FP8_LINEAR, 2, 256, 6144, 0) == 0      # quantized inside the kernel
+    assert call(ws=None) == W.ERR_NULL
+    assert call(ws=U) == W.ERR_ALIGN
+    assert call(nws=16) == W.ERR_WORKSPACE
     assert call(M=0) == W.ERR_SHAPE
     assert call(M=17) == W.ERR_SHAPE
     assert call(N=24) == W.ERR_SHAPE                            # N % 16
@@ -192,6 +196,6 @@ def test_fp8_linear_w8a8_validation(L):
     assert call(s_w=-1.0) == W.ERR_ARG
     assert call(s_w=float("nan")) == W.ERR_ARG
     assert call(x=None) == W.ERR_NULL
-    assert call(ws=None) == W.ERR_NULL
+    assert call(w=None) == W.ERR_NULL
     assert call(y=U) == W.ERR_ALIGN
-    assert call(nws=16) == W.ERR_WORKSPACE
+    assert call(x=U) == W.ERR_ALIGN

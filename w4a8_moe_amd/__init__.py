@@ -332,10 +332,11 @@ def fp8_linear_w8a8(x, s_x, w, s_w, out=None, ws=None):
     _need(w, torch.uint8, (N, K), "w")
     y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=x.device)
     nws = workspace_bytes(OP_FP8_LINEAR, M, N, K, 0)
-    if ws is None or ws.numel() < nws:
+    if nws > 0 and (ws is None or ws.numel() < nws):
         ws = _workspace(nws, x.device)
     _check("fp8_linear_w8a8", lib().fp8_linear_w8a8(_ptr(x), float(s_x), _ptr(w), float(s_w), M, N, K, _ptr(y),
-                                                    _ptr(ws), ws.numel(), _stream(x.device)))
+                                                    _ptr(ws) if nws > 0 else None, ws.numel() if nws > 0 else 0,
+                                                    _stream(x.device)))
     return y
 
 

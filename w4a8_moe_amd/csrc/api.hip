@@ -89,7 +89,7 @@ size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t 
     case W4A8_OP_TENSOR_QUANT:
       return (size_t)kTensorQuantParts * sizeof(uint32_t);
     case W4A8_OP_FP8_LINEAR:
-      if (T_or_M < 1 || I_or_K < 1) return 0;
+      if (T_or_M < 1 || I_or_K < 1 || fp8_linear_quant_inside(T_or_M)) return 0;
       return round_up((size_t)T_or_M * (size_t)I_or_K, 256);   // the activation codes
     default:
       return 0;
@@ -283,18 +283,19 @@ int32_t fp8_tensor_quant(const uint16_t* w_bf16, int64_t n, uint8_t* w_e4m3, flo
 
 int32_t fp8_linear_w8a8(const uint16_t* x_bf16, float s_x, const uint8_t* w_e4m3, float s_w, int32_t M, int32_t N,
                         int32_t K, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* stream) {
-  if (!x_bf16 || !w_e4m3 || !y_bf16 || !ws) return W4A8_ERR_NULL;
+  if (!x_bf16 || !w_e4m3 || !y_bf16) return W4A8_ERR_NULL;
   if (M < 1 || M > 16 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return W4A8_ERR_SHAPE;
   if ((int64_t)N * K >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
   if ((int64_t)M * K > 65536) return W4A8_ERR_UNSUPPORTED;       // activation codes staged in 64 KB of LDS
   if (!good_scale(s_x) || !std::isfinite(s_w) || s_w < 0.0f) return W4A8_ERR_ARG;
-  if (!aligned16(x_bf16) || !aligned16(w_e4m3) || !aligned16(y_bf16) || !aligned16(ws)) return W4A8_ERR_ALIGN;
-  if (ws_bytes < w4a8_workspace_bytes(W4A8_OP_FP8_LINEAR, M, N, K, 0)) return W4A8_ERR_WORKSPACE;
-  uint8_t* xq = static_cast<uint8_t*>(ws);
-  const hipStream_t st = as_stream(stream);
-  launch_fp8_quant(x_bf16, (int64_t)M * K, s_x, xq, st);
-  if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;
-  launch_fp8_linear(xq, w_e4m3, s_x * s_w, M, N, K, y_bf16, st);
+  if (!aligned16(x_bf16) || !aligned16(w_e4m3) || !aligned16(y_bf16)) return W4A8_ERR_ALIGN;
+  const size_t need = w4a8_workspace_bytes(W4A8_OP_FP8_LINEAR, M, N, K, 0);
+  if (need > 0) {
+    if (!ws) return W4A8_ERR_NULL;
+    if (!aligned16(ws)) return W4A8_ERR_ALIGN;
+    if (ws_bytes < need) return W4A8_ERR_WORKSPACE;
+  }
+  launch_fp8_linear(x_bf16, s_x, static_cast<uint8_t*>(ws), w_e4m3, s_x * s_w, M, N, K, y_bf16, as_stream(stream));
   return launch_status();
 }
 

@@ -24,9 +24,10 @@
 //
 // The per-tensor FP8 linear (fp8_linear_kernel, the dense projections of the W4A8 model:
 // quant_method "fp8" with static activations on the page "ROCm: enable trillion-parameter
-// MoE models with INT4-FP8 single node") has the same mapping; its activations arrive as
-// E4M3 codes and are staged as bytes (M x K in LDS, half the bf16 size), both operands are
-// widened to bf16 in registers (exact), and the one scale s_x * s_w multiplies the sum.
+// MoE models with INT4-FP8 single node") has the same mapping; its activations are
+// quantized with their static scale (inside the kernel for M <= 2), staged as E4M3 bytes
+// (M x K in LDS, half the bf16 size), both operands are widened to bf16 in registers
+// (exact), and the one scale s_x * s_w multiplies the sum.
 #include <algorithm>
 
 #include "common.h"
@@ -171,10 +172,14 @@ void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s
 // y[m][n] = bf16( scale * sum_k dec(xq[m][k]) * dec(W[n][k]) ), scale = s_x * s_w.
 // Staged unit (kb, j, g, m) = 8 codes of x[m][kb*128 + g*32 + j*8 .. +8] at byte
 // ((((kb*4 + j)*4 + g)*M + m) << 3): lane (m, g) of MFMA j reads 8 contiguous bytes.
-template <int RB>   // 16-row blocks per workgroup
+// With QUANT, every workgroup quantizes the M x K activations itself while staging them
+// (the arithmetic of fp8_quant_static: correctly rounded x / s_x, nearest even,
+// saturated), and the call is one launch: measured faster for M <= 2. For more rows the
+// quantization runs once, in its own launch, and the kernel stages its codes (xq).
+template <int RB, bool QUANT>   // 16-row blocks per workgroup; quantize x in the kernel
 __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
-    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
-    uint16_t* __restrict__ y) {
+    const uint16_t* __restrict__ x, float s_x, const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w,
+    float scale, int M, int N, int K, uint16_t* __restrict__ y) {
   constexpr int kWaves = RB * kBlSplit;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -184,8 +189,14 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
     const int m = u / (K >> 3), c8 = u - m * (K >> 3);
     const int kb = c8 >> 4, within = c8 & 15;
     const int g = within >> 2, j = within & 3;
-    const uint2 v = *reinterpret_cast<const uint2*>(xq + (size_t)m * K + c8 * 8);
-    *reinterpret_cast<uint2*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 3)) = v;
+    uint2 codes;
+    if (QUANT) {
+      const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + c8 * 8);
+      codes = make_uint2(quant4_e4m3(v.x, v.y, s_x), quant4_e4m3(v.z, v.w, s_x));
+    } else {
+      codes = *reinterpret_cast<const uint2*>(xq + (size_t)m * K + c8 * 8);
+    }
+    *reinterpret_cast<uint2*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 3)) = codes;
   }
   __syncthreads();
   const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);
@@ -251,19 +262,25 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
   *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
 }
 
-template <int RB>
-static void launch_fl(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
-                      hipStream_t st) {
+template <int RB, bool QUANT>
+static void launch_fl(const uint16_t* x, float s_x, const uint8_t* xq, const uint8_t* w, float scale, int M, int N,
+                      int K, uint16_t* y, hipStream_t st) {
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
   const size_t lds = std::max((size_t)M * K, (size_t)(RB * kBlSplit - 1) * kWave * sizeof(v4f));
-  hipLaunchKernelGGL(fp8_linear_kernel<RB>, dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w, scale, M, N,
-                     K, y);
+  hipLaunchKernelGGL((fp8_linear_kernel<RB, QUANT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, x, s_x, xq,
+                     w, scale, M, N, K, y);
 }
 
-void launch_fp8_linear(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
-                       hipStream_t st) {
-  if (M <= 2) launch_fl<W4A8_BL_RB_SMALL_M>(xq, w, scale, M, N, K, y, st);
-  else launch_fl<W4A8_BL_RB_LARGE_M>(xq, w, scale, M, N, K, y, st);
+bool fp8_linear_quant_inside(int M) { return M <= 2; }
+
+void launch_fp8_linear(const uint16_t* x, float s_x, uint8_t* xq, const uint8_t* w, float scale, int M, int N,
+                       int K, uint16_t* y, hipStream_t st) {
+  if (fp8_linear_quant_inside(M)) {
+    launch_fl<W4A8_BL_RB_SMALL_M, true>(x, s_x, nullptr, w, scale, M, N, K, y, st);
+  } else {
+    launch_fp8_quant(x, (int64_t)M * K, s_x, xq, st);
+    launch_fl<W4A8_BL_RB_LARGE_M, false>(nullptr, s_x, xq, w, scale, M, N, K, y, st);
+  }
 }
 
 }  // namespace w4a8

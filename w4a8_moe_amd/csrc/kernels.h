@@ -83,8 +83,10 @@ void launch_combine(const float* partial, int ksplit, int P, int H, const int32_
 // ---- block_linear.hip
 void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K,
                              uint16_t* y, hipStream_t st);
-// per-tensor FP8 linear on E4M3 activation codes: y = bf16(scale * sum_k xq * wq)
-void launch_fp8_linear(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
-                       hipStream_t st);
+// per-tensor FP8 linear: xq = e4m3(x / s_x), y = bf16(scale * sum_k xq * wq); xq (M * K
+// bytes of workspace) is used unless fp8_linear_quant_inside(M), where the kernel quantizes
+bool fp8_linear_quant_inside(int M);
+void launch_fp8_linear(const uint16_t* x, float s_x, uint8_t* xq, const uint8_t* w, float scale, int M, int N,
+                       int K, uint16_t* y, hipStream_t st);
 
 }  // namespace w4a8
