@@ -172,6 +172,9 @@ LAYER_CASES = [
     synth.custom_moe("three_tiles", T=40, H=512, I=512, E=3, act=synth.ACT_GELU_TANH, w_cfg=203, x_cfg=203),
     synth.custom_moe("one_token", T=1, H=256, I=256, E=8, w_cfg=204, x_cfg=204),
     synth.custom_moe("many_experts", T=24, H=256, I=384, E=32, w_cfg=205, x_cfg=205, out_f32=False),
+    # the largest expert count the calls accept: 256 experts, at most 48 of them routed to
+    synth.custom_moe("max_experts", T=24, H=128, I=128, E=256, w_cfg=206, x_cfg=206, out_f32=False,
+                     logit_sigma=2.0),
 ]
 
 
@@ -214,6 +217,9 @@ def test_moe_layer_parity(cfg):
 # (ragged last tiles, empty experts), 128-channel gate|up tiles, 256-channel down tiles.
 PREFILL_CASES = [
     synth.custom_moe("pf_small", T=96, H=256, I=512, E=4, w_cfg=301, x_cfg=301),
+    # the fewest tokens that take the tiled kernel (64 take the streaming one)
+    synth.custom_moe("pf_first_tiled", T=65, H=384, I=256, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=307,
+                     x_cfg=307, logit_sigma=1.5),
     synth.custom_moe("pf_ragged", T=300, H=640, I=384, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=302,
                      x_cfg=302, logit_sigma=1.5),
     synth.custom_moe("pf_multi_tile", T=700, H=1152, I=1280, E=2, w_cfg=303, x_cfg=303),
@@ -306,3 +312,16 @@ def test_fp8_block_linear_parity(M, N, K):
     assert_final_close(bf16_bits_to_f64(host(y)), bf16_bits_to_f64(y_bits))
     y2 = W.fp8_block_linear(bf16_dev(x), u8_dev(codes), f32_dev(S))
     assert torch().equal(y, y2)
+
+
+def test_empty_batch():
+    """No tokens: every call returns OK and enqueues nothing; the layer's output is empty."""
+    t = torch()
+    cfg = synth.custom_moe("empty", T=1, H=256, I=256, E=8, w_cfg=208, x_cfg=208, out_f32=False)
+    w13, s13 = W.w4_pack(bf16_dev(synth.moe_weights(cfg, "w13")), tiled=True)
+    w2, s2 = W.w4_pack(bf16_dev(synth.moe_weights(cfg, "w2")), tiled=True)
+    x = t.empty((0, cfg.H), dtype=t.bfloat16, device="cuda")
+    logits = t.empty((0, cfg.E), dtype=t.float32, device="cuda")
+    out = W.moe_layer(x, 0.01, logits, w13, s13, w2, s2, cfg.act, 0.05)
+    t.cuda.synchronize()
+    assert tuple(out.shape) == (0, cfg.H)
