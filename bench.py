@@ -191,6 +191,25 @@ def bench_fp8_linear(torch, W, dev, reps=16, iters=50):
     return out
 
 
+def copy_bandwidth(torch, dev, nbytes=1 << 30, iters=10):
+    """A plain device-to-device copy of 1 GiB (read + write bytes per second): the
+    measured reference beside the 8 TB/s published peak."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(st)
+    for _ in range(iters):
+        dst.copy_(src)
+    ev[1].record(st)
+    torch.cuda.synchronize()
+    s = ev[0].elapsed_time(ev[1]) * 1e-3 / iters
+    del src, dst
+    return 2 * nbytes / s / 1e9
+
+
 def measure_layer(torch, W, cfg, steps, warmup):
     """One workload: pack, graph-captured steps, the timed region, per-call durations.
     Returns the JSON fields of the workload and the routing ids (for the CPU baseline)."""
@@ -364,6 +383,10 @@ def main():
         result["prefill"] = {k: pf[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
                                                  "layer_mfma_frac", "calls_us", "roofline")}
         torch.cuda.empty_cache()
+    if result["roofline"]["bound"] == "hbm":
+        cb = copy_bandwidth(torch, dev)
+        result["hbm_copy_ref"] = {"GB/s": round(cb, 1), "of_peak": round(cb / HBM_PEAK_GBS, 4),
+                                  "gemm1_frac_of_copy": round(result["roofline"]["achieved"] / cb, 4)}
     if args.copy_ref:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
