@@ -325,3 +325,22 @@ def test_empty_batch():
     out = W.moe_layer(x, 0.01, logits, w13, s13, w2, s2, cfg.act, 0.05)
     t.cuda.synchronize()
     assert tuple(out.shape) == (0, cfg.H)
+
+
+@pytest.mark.parametrize("sizes", [(10240, 6144), (12288, 512, 512)])
+def test_fp8_block_fused_groups(sizes):
+    """The fusion groups of the block-FP8 projections (whole numbers of 128-row blocks):
+    quantizing the fused weight equals quantizing the groups and concatenating rows and
+    scales, and the fused GEMV's outputs equal the groups' GEMVs side by side, bit for bit
+    (each 16-row block is reduced on its own, in the same order)."""
+    K, M = 512, 8
+    parts = [synth.block_weights(synth.custom_block(f"gg{i}", M=1, N=n, K=K, cfg=77, sub=i))
+             for i, n in enumerate(sizes)]
+    qf, Sf = W.fp8_block_quant(bf16_dev(np.concatenate(parts, axis=0)))
+    qs = [W.fp8_block_quant(bf16_dev(p)) for p in parts]
+    assert torch().equal(qf, torch().cat([q for q, _ in qs], 0))
+    assert torch().equal(Sf, torch().cat([S for _, S in qs], 0))
+    x = bf16_dev(synth.block_activations(synth.custom_block("ggx", M=M, N=16, K=K, cfg=78)))
+    yf = W.fp8_block_linear(x, qf, Sf)
+    ys = torch().cat([W.fp8_block_linear(x, q, S) for q, S in qs], 1)
+    assert torch().equal(yf, ys)

@@ -78,3 +78,24 @@ def test_page_shapes(golden_dir):
     assert synth.GROK_PREFILL.T == g["prefill"]["batch"] * g["prefill"]["input_len"]
     for c in synth.BLOCK_CONFIGS.values():
         assert [c.N, c.K] in [item["weight"] for item in g["block_fp8"]]
+
+
+def test_fused_groups_concatenate_exactly():
+    """Page C: every fp8 fusion group is a whole number of 128-row blocks (10240 / 6144 for
+    in_proj_qkvz, 12288 / 512 / 512 for qkv), so quantizing the groups apart and
+    concatenating rows and block scales gives the fused tensor's quantization, and the
+    fused projection's outputs are the groups' outputs side by side."""
+    for sizes, sub in (((10240, 6144), 0), ((12288, 512, 512), 1)):
+        K = 256
+        parts = [synth.block_weights(synth.custom_block(f"grp{sub}_{i}", M=1, N=n, K=K, cfg=75, sub=10 * sub + i))
+                 for i, n in enumerate(sizes)]
+        fused = np.concatenate(parts, axis=0)
+        qf, Sf = fp8_block_quantize(fused)
+        qs = [fp8_block_quantize(p) for p in parts]
+        assert np.array_equal(qf, np.concatenate([q for q, _ in qs], axis=0))
+        assert np.array_equal(Sf, np.concatenate([S for _, S in qs], axis=0))
+        assert Sf.shape == (sum(sizes) // 128, K // 128)
+        x = synth.block_activations(synth.custom_block("grpx", M=2, N=16, K=K, cfg=76))
+        yf, _ = fp8_block_linear(x, qf, Sf)
+        ys = np.concatenate([fp8_block_linear(x, q, S)[0] for q, S in qs], axis=1)
+        assert np.array_equal(yf, ys)
