@@ -266,15 +266,16 @@ int32_t fp8_tensor_quant(const uint16_t* w_bf16, int64_t n, uint8_t* w_e4m3, flo
  * fp8_linear_w8a8 -- per-tensor static FP8 dense linear for decode rows (the same two
  *   pages; activation_scheme static):
  *   xq = e4m3(fp32(x / s_x)) (the arithmetic of fp8_quant_static; in the linear's own
- *   kernel for M <= 2, else in a launch of its own into the workspace), then
+ *   kernel for M <= 2 with M * K <= 65536, else in a launch of its own into the
+ *   workspace), then
  *   y[m][n] = bf16( fp32(s_x * s_w) * sum_k dec(xq[m][k]) * dec(w[n][k]) ), nearest even;
  *   the products are exact and summed in fp32.
  *   x_bf16 [M][K], s_x > 0 (static activation scale, host value), w_e4m3 [N][K] with its
  *   tensor scale s_w >= 0 (host value), y_bf16 [M][N] (out).
- *   Requires 1 <= M <= 16, N % 16 == 0, K % 128 == 0; M * K <= 65536 (the codes of x are
- *   staged in LDS; W4A8_ERR_UNSUPPORTED above).
+ *   Requires 1 <= M <= 64, N % 16 == 0, K % 128 == 0. Up to 16 rows with M * K <= 65536
+ *   the codes of x are staged whole in LDS; otherwise they are staged in chunks of K.
  *   Workspace: w4a8_workspace_bytes(W4A8_OP_FP8_LINEAR, M, N, K, 0) bytes: 0 for M <= 2
- *   (ws may be NULL), else M * K rounded up to 256 (holds xq).
+ *   with M * K <= 65536 (ws may be NULL), else M * K rounded up to 256 (holds xq).
  */
 int32_t fp8_linear_w8a8(const uint16_t* x_bf16, float s_x, const uint8_t* w_e4m3, float s_w,
                         int32_t M, int32_t N, int32_t K, uint16_t* y_bf16,

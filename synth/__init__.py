@@ -93,16 +93,19 @@ BLOCK_QKV_M8 = BlockConfig("block_qkv_m8", M=8, N=13312, K=2560, sub=1)
 # Per-tensor FP8 (W8A8) dense projections of the Grok-1 attention block (page "ROCm:
 # enable trillion-parameter MoE models with INT4-FP8 single node": hidden 6144, 48 query
 # heads and 8 key/value heads of 128): the fused q|k|v projection [6144 + 2 * 1024, 6144]
-# and the output projection [6144, 6144], decode rows M in {1, 8}.
+# and the output projection [6144, 6144], decode rows M in {1, 8, 32} (32: the batch of the
+# page's bench command).
 FP8_QKV_M1 = BlockConfig("fp8_qkv_m1", M=1, N=8192, K=6144, cfg=7, sub=0)
 FP8_QKV_M8 = BlockConfig("fp8_qkv_m8", M=8, N=8192, K=6144, cfg=7, sub=0)
 FP8_O_M1 = BlockConfig("fp8_o_m1", M=1, N=6144, K=6144, cfg=7, sub=1)
 FP8_O_M8 = BlockConfig("fp8_o_m8", M=8, N=6144, K=6144, cfg=7, sub=1)
+FP8_QKV_M32 = BlockConfig("fp8_qkv_m32", M=32, N=8192, K=6144, cfg=7, sub=0)   # the page's decode batch of 32
+FP8_O_M32 = BlockConfig("fp8_o_m32", M=32, N=6144, K=6144, cfg=7, sub=1)
 
 MOE_CONFIGS = {c.name: c for c in (TINY, MIXTRAL_DECODE, GROK_DECODE, GROK_PREFILL, GROK_TP8_DECODE,
                                    GROK_TP8_PREFILL)}
 BLOCK_CONFIGS = {c.name: c for c in (BLOCK_QKVZ_M1, BLOCK_QKVZ_M8, BLOCK_QKV_M1, BLOCK_QKV_M8)}
-LINEAR_CONFIGS = {c.name: c for c in (FP8_QKV_M1, FP8_QKV_M8, FP8_O_M1, FP8_O_M8)}
+LINEAR_CONFIGS = {c.name: c for c in (FP8_QKV_M1, FP8_QKV_M8, FP8_QKV_M32, FP8_O_M1, FP8_O_M8, FP8_O_M32)}
 
 
 def custom_moe(name, T, H, I, E, act=ACT_SILU, w_sigma=0.02, logit_sigma=1.0,

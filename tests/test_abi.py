@@ -188,10 +188,10 @@ def test_fp8_linear_w8a8_validation(L):
     assert call(ws=U) == W.ERR_ALIGN
     assert call(nws=16) == W.ERR_WORKSPACE
     assert call(M=0) == W.ERR_SHAPE
-    assert call(M=17) == W.ERR_SHAPE
+    assert call(M=65) == W.ERR_SHAPE
     assert call(N=24) == W.ERR_SHAPE                            # N % 16
     assert call(K=192) == W.ERR_SHAPE                           # K % 128
-    assert call(M=16, K=8192) == W.ERR_UNSUPPORTED              # M * K > 65536
+    assert W.workspace_bytes(W.OP_FP8_LINEAR, 2, 256, 65536, 0) == 2 * 65536   # past the fused size
     assert call(s_x=0.0) == W.ERR_ARG
     assert call(s_w=-1.0) == W.ERR_ARG
     assert call(s_w=float("nan")) == W.ERR_ARG

@@ -45,7 +45,11 @@ def test_integer_case_bit_exact():
 # larger N: up to 2 rows the activations are quantized inside the kernel (2 row blocks per
 # workgroup), above that in a launch of their own (4 row blocks per workgroup)
 @pytest.mark.parametrize("M,N,K", [(1, 256, 384), (8, 400, 256), (16, 128, 4096), (3, 1024, 6144), (10, 48, 6144),
-                                   (2, 16, 128), (4, 16384, 256), (2, 8192, 384), (8, 8192, 256)])
+                                   (2, 16, 128), (4, 16384, 256), (2, 8192, 384), (8, 8192, 256),
+                                   # activations staged in chunks of K: more than 16 rows (up to 64, ragged
+                                   # tiles), or M * K past 64 KB, or a ragged last K-quarter
+                                   (32, 1024, 6144), (32, 6144, 768), (64, 512, 2560), (20, 256, 6144),
+                                   (17, 128, 128), (16, 256, 8192), (2, 64, 33024), (48, 96, 1152)])
 def test_fp8_linear_parity(M, N, K):
     cfg = synth.custom_block("fl", M=M, N=N, K=K, cfg=93, sub=N)
     w = synth.block_weights(cfg)

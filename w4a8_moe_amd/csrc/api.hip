@@ -89,7 +89,8 @@ size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t 
     case W4A8_OP_TENSOR_QUANT:
       return (size_t)kTensorQuantParts * sizeof(uint32_t);
     case W4A8_OP_FP8_LINEAR:
-      if (T_or_M < 1 || I_or_K < 1 || fp8_linear_quant_inside(T_or_M)) return 0;
+      if (T_or_M < 1 || I_or_K < 1) return 0;
+      if (fp8_linear_quant_inside(T_or_M) && (int64_t)T_or_M * I_or_K <= 65536) return 0;
       return round_up((size_t)T_or_M * (size_t)I_or_K, 256);   // the activation codes
     default:
       return 0;
@@ -284,9 +285,8 @@ int32_t fp8_tensor_quant(const uint16_t* w_bf16, int64_t n, uint8_t* w_e4m3, flo
 int32_t fp8_linear_w8a8(const uint16_t* x_bf16, float s_x, const uint8_t* w_e4m3, float s_w, int32_t M, int32_t N,
                         int32_t K, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* stream) {
   if (!x_bf16 || !w_e4m3 || !y_bf16) return W4A8_ERR_NULL;
-  if (M < 1 || M > 16 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return W4A8_ERR_SHAPE;
-  if ((int64_t)N * K >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
-  if ((int64_t)M * K > 65536) return W4A8_ERR_UNSUPPORTED;       // activation codes staged in 64 KB of LDS
+  if (M < 1 || M > 64 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return W4A8_ERR_SHAPE;
+  if ((int64_t)N * K >= (int64_t(1) << 40) || (int64_t)M * K >= (int64_t(1) << 31)) return W4A8_ERR_SHAPE;
   if (!good_scale(s_x) || !std::isfinite(s_w) || s_w < 0.0f) return W4A8_ERR_ARG;
   if (!aligned16(x_bf16) || !aligned16(w_e4m3) || !aligned16(y_bf16)) return W4A8_ERR_ALIGN;
   const size_t need = w4a8_workspace_bytes(W4A8_OP_FP8_LINEAR, M, N, K, 0);

@@ -262,6 +262,124 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
   *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
 }
 
+// Up to 64 rows, any K: the same mapping (four waves per 16-row block, one K-quarter each),
+// with NT 16-column tiles of rows per weight block, and the activation codes staged chunk
+// by chunk: all waves walk their quarters in step, kChunkKB 128-K blocks at a time, and a
+// chunk holds those blocks of all four quarters for all rows (4 x 64 x 256 codes = 64 KB).
+// Unit (q, cb, j, g, m) = 8 codes of row m at K = (q*per + c*kChunkKB + cb)*128 + g*32 + j*8,
+// at byte (((((q*kChunkKB + cb)*4 + j)*4 + g)*Mp + m) << 3), Mp = 16 * NT.
+constexpr int kChunkKB = 2;
+
+template <int RB, int NT>
+__global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
+    uint16_t* __restrict__ y) {
+  constexpr int kWaves = RB * kBlSplit, Mp = 16 * NT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int KB = K >> 7;
+  const int per = (KB + kBlSplit - 1) / kBlSplit;           // 128-K blocks per quarter (the last may be short)
+  const int chunks = (per + kChunkKB - 1) / kChunkKB;
+  const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);
+  const bool rb_ok = blockIdx.x * RB + wave / kBlSplit < N / 16;
+  const int part_k = wave % kBlSplit;
+  const int i = lane & 15, g = lane >> 4;
+  const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
+  const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
+
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0;
+  if (kb_begin < kb_end) {
+    q0 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128);
+    q1 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128 + 16);
+  }
+  const int units = kBlSplit * kChunkKB * 16 * M;            // 8-code units of one chunk
+  for (int c = 0; c < chunks; ++c) {
+    if (c > 0) lds_barrier();                                // every wave is done with chunk c - 1
+    for (int u = tid; u < units; u += kWaves * kWave) {
+      const int m = u % M, r = u / M;                        // r = ((q*kChunkKB + cb)*16 + g*4 + j)
+      const int jg = r & 15, qcb = r >> 4;
+      const int gg = jg >> 2, jj = jg & 3, cb = qcb % kChunkKB, q = qcb / kChunkKB;
+      const int kb = q * per + c * kChunkKB + cb;
+      uint2 v = make_uint2(0u, 0u);
+      if (kb < min(KB, (q + 1) * per) && c * kChunkKB + cb < per)
+        v = *reinterpret_cast<const uint2*>(xq + (size_t)m * K + kb * 128 + gg * 32 + jj * 8);
+      *reinterpret_cast<uint2*>(lds + (((((q * kChunkKB + cb) * 4 + jj) * 4 + gg) * Mp + m) << 3)) = v;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int cb = 0; cb < kChunkKB; ++cb) {
+      const int kb = kb_begin + c * kChunkKB + cb;
+      if (kb < kb_end) {
+        const uint4 a0 = q0, a1 = q1;
+        if (kb + 1 < kb_end) {
+          q0 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128);
+          q1 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128 + 16);
+        }
+        const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t d0, d1, d2, d3;
+          e4m3x4_to_bf16x4(cw[2 * j], d0, d1);
+          e4m3x4_to_bf16x4(cw[2 * j + 1], d2, d3);
+          const v8bf a = bf16_operand(d0, d1, d2, d3);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int m = t * 16 + i;
+            uint2 bx = make_uint2(0u, 0u);
+            if (m < M)
+              bx = *reinterpret_cast<const uint2*>(
+                  lds + (((((part_k * kChunkKB + cb) * 4 + j) * 4 + g) * Mp + m) << 3));
+            uint32_t e0, e1, e2, e3;
+            e4m3x4_to_bf16x4(bx.x, e0, e1);
+            e4m3x4_to_bf16x4(bx.y, e2, e3);
+            acc[t] = mfma_bf16_16x16x32(a, bf16_operand(e0, e1, e2, e3), acc[t]);
+          }
+        }
+      }
+    }
+  }
+  // partial sums of a row block's waves, added in K-part order over the staged codes
+  v4f* part = reinterpret_cast<v4f*>(lds);
+  __syncthreads();
+  if (part_k > 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) part[((wave - 1) * NT + t) * kWave + lane] = acc[t];
+  }
+  __syncthreads();
+  if (part_k > 0 || !rb_ok) return;
+  const int n = rb * 16 + 4 * g;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = t * 16 + i;
+    v4f a = acc[t];
+#pragma unroll
+    for (int v = 1; v < kBlSplit; ++v) {
+      const v4f o = part[((wave + v - 1) * NT + t) * kWave + lane];
+      a[0] += o[0]; a[1] += o[1]; a[2] += o[2]; a[3] += o[3];
+    }
+    if (m < M) {
+      uint2 o;
+      o.x = f32_to_bf16_bits(scale * a[0]) | f32_to_bf16_bits(scale * a[1]) << 16;
+      o.y = f32_to_bf16_bits(scale * a[2]) | f32_to_bf16_bits(scale * a[3]) << 16;
+      *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = o;
+    }
+  }
+}
+
+template <int NT>
+static void launch_flw(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
+                       hipStream_t st) {
+  constexpr int RB = 2;
+  const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
+  const size_t lds = std::max((size_t)kBlSplit * kChunkKB * 128 * 16 * NT,
+                              (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f));
+  hipLaunchKernelGGL((fp8_linear_wide_kernel<RB, NT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w,
+                     scale, M, N, K, y);
+}
+
 template <int RB, bool QUANT>
 static void launch_fl(const uint16_t* x, float s_x, const uint8_t* xq, const uint8_t* w, float scale, int M, int N,
                       int K, uint16_t* y, hipStream_t st) {
@@ -273,14 +391,20 @@ static void launch_fl(const uint16_t* x, float s_x, const uint8_t* xq, const uin
 
 bool fp8_linear_quant_inside(int M) { return M <= 2; }
 
+// the whole activation in LDS (M <= 16, M * K <= 65536), else the chunked kernel
+static bool fp8_linear_whole_x(int M, int K) { return M <= 16 && (int64_t)M * K <= 65536; }
+
 void launch_fp8_linear(const uint16_t* x, float s_x, uint8_t* xq, const uint8_t* w, float scale, int M, int N,
                        int K, uint16_t* y, hipStream_t st) {
-  if (fp8_linear_quant_inside(M)) {
+  if (fp8_linear_quant_inside(M) && fp8_linear_whole_x(M, K)) {
     launch_fl<W4A8_BL_RB_SMALL_M, true>(x, s_x, nullptr, w, scale, M, N, K, y, st);
-  } else {
-    launch_fp8_quant(x, (int64_t)M * K, s_x, xq, st);
-    launch_fl<W4A8_BL_RB_LARGE_M, false>(nullptr, s_x, xq, w, scale, M, N, K, y, st);
+    return;
   }
+  launch_fp8_quant(x, (int64_t)M * K, s_x, xq, st);
+  if (fp8_linear_whole_x(M, K)) launch_fl<W4A8_BL_RB_LARGE_M, false>(nullptr, s_x, xq, w, scale, M, N, K, y, st);
+  else if (M <= 16) launch_flw<1>(xq, w, scale, M, N, K, y, st);
+  else if (M <= 32) launch_flw<2>(xq, w, scale, M, N, K, y, st);
+  else launch_flw<4>(xq, w, scale, M, N, K, y, st);
 }
 
 }  // namespace w4a8
