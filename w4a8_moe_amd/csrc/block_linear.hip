@@ -264,17 +264,15 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
 
 // Up to 64 rows, any K: the same mapping (four waves per 16-row block, one K-quarter each),
 // with NT 16-column tiles of rows per weight block, and the activation codes staged chunk
-// by chunk: all waves walk their quarters in step, kChunkKB 128-K blocks at a time, and a
-// chunk holds those blocks of all four quarters for all rows (4 x 64 x 256 codes = 64 KB).
-// Unit (q, cb, j, g, m) = 8 codes of row m at K = (q*per + c*kChunkKB + cb)*128 + g*32 + j*8,
-// at byte (((((q*kChunkKB + cb)*4 + j)*4 + g)*Mp + m) << 3), Mp = 16 * NT.
-constexpr int kChunkKB = 2;
-
+// by chunk: all waves walk their quarters in step, CK 128-K blocks at a time, and a chunk
+// holds those blocks of all four quarters for all rows (64 KB: CK = 8 / NT, so 8, 4 or 2).
+// Unit (q, cb, j, g, m) = 8 codes of row m at K = (q*per + c*CK + cb)*128 + g*32 + j*8, at
+// byte (((((q*CK + cb)*4 + j)*4 + g)*Mp + m) << 3), Mp = 16 * NT.
 template <int RB, int NT>
 __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
     uint16_t* __restrict__ y) {
-  constexpr int kWaves = RB * kBlSplit, Mp = 16 * NT;
+  constexpr int kWaves = RB * kBlSplit, Mp = 16 * NT, kChunkKB = 8 / NT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int KB = K >> 7;
@@ -374,7 +372,7 @@ static void launch_flw(const uint8_t* xq, const uint8_t* w, float scale, int M, 
                        hipStream_t st) {
   constexpr int RB = 2;
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
-  const size_t lds = std::max((size_t)kBlSplit * kChunkKB * 128 * 16 * NT,
+  const size_t lds = std::max((size_t)kBlSplit * (8 / NT) * 128 * 16 * NT,
                               (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f));
   hipLaunchKernelGGL((fp8_linear_wide_kernel<RB, NT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w,
                      scale, M, N, K, y);
