@@ -240,7 +240,8 @@ int32_t fp8_block_quant(const uint16_t* w_bf16, int32_t N, int32_t K,
  * fp8_block_linear -- block-FP8 weight-only decode GEMV/GEMM (same page): x stays bf16,
  *   y[m][n] = bf16( sum_kb S[n/128][kb] * sum_{k in block kb} x[m][k] * W[n][k] )
  *   x_bf16 [M][K], w_e4m3 [N][K], s [ceil(N/128)][K/128] fp32, y_bf16 [M][N] (out).
- * Requires 1 <= M <= 16, N % 16 == 0, K % 128 == 0.
+ * Requires 1 <= M <= 64, N % 16 == 0, K % 128 == 0. Up to 16 rows with M * K * 2 <=
+ * 65536 the activations are staged whole in LDS; otherwise in chunks of K.
  * Workspace: w4a8_workspace_bytes(W4A8_OP_BLOCK_LINEAR, M, N, K, 0) (currently 0).
  */
 int32_t fp8_block_linear(const uint16_t* x_bf16, const uint8_t* w_e4m3, const float* s,

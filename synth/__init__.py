@@ -89,6 +89,8 @@ BLOCK_QKVZ_M1 = BlockConfig("block_qkvz_m1", M=1, N=16384, K=2560, sub=0)
 BLOCK_QKVZ_M8 = BlockConfig("block_qkvz_m8", M=8, N=16384, K=2560, sub=0)
 BLOCK_QKV_M1 = BlockConfig("block_qkv_m1", M=1, N=13312, K=2560, sub=1)
 BLOCK_QKV_M8 = BlockConfig("block_qkv_m8", M=8, N=13312, K=2560, sub=1)
+BLOCK_QKVZ_M32 = BlockConfig("block_qkvz_m32", M=32, N=16384, K=2560, sub=0)   # small-batch decode
+BLOCK_QKV_M32 = BlockConfig("block_qkv_m32", M=32, N=13312, K=2560, sub=1)
 
 # Per-tensor FP8 (W8A8) dense projections of the Grok-1 attention block (page "ROCm:
 # enable trillion-parameter MoE models with INT4-FP8 single node": hidden 6144, 48 query
@@ -104,7 +106,8 @@ FP8_O_M32 = BlockConfig("fp8_o_m32", M=32, N=6144, K=6144, cfg=7, sub=1)
 
 MOE_CONFIGS = {c.name: c for c in (TINY, MIXTRAL_DECODE, GROK_DECODE, GROK_PREFILL, GROK_TP8_DECODE,
                                    GROK_TP8_PREFILL)}
-BLOCK_CONFIGS = {c.name: c for c in (BLOCK_QKVZ_M1, BLOCK_QKVZ_M8, BLOCK_QKV_M1, BLOCK_QKV_M8)}
+BLOCK_CONFIGS = {c.name: c for c in (BLOCK_QKVZ_M1, BLOCK_QKVZ_M8, BLOCK_QKVZ_M32, BLOCK_QKV_M1, BLOCK_QKV_M8,
+                                     BLOCK_QKV_M32)}
 LINEAR_CONFIGS = {c.name: c for c in (FP8_QKV_M1, FP8_QKV_M8, FP8_QKV_M32, FP8_O_M1, FP8_O_M8, FP8_O_M32)}
 
 

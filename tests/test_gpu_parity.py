@@ -301,7 +301,11 @@ def test_fp8_block_quant_bit_exact(N, K):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 256, 384), (8, 400, 256), (16, 128, 2048), (3, 1024, 2560), (12, 64, 2560),
-                                   (2, 48, 384), (5, 80, 1152), (1, 16, 128)])
+                                   (2, 48, 384), (5, 80, 1152), (1, 16, 128),
+                                   # activations staged in chunks of K: more than 16 rows (up to 64, ragged
+                                   # tiles), or more than 64 KB of them, or a ragged last K-quarter
+                                   (32, 256, 2560), (64, 128, 1024), (20, 512, 2560), (16, 256, 4096),
+                                   (48, 80, 1152), (2, 64, 16512), (17, 144, 128)])
 def test_fp8_block_linear_parity(M, N, K):
     cfg = synth.custom_block("bl", M=M, N=N, K=K, cfg=400 + M)
     w = synth.block_weights(cfg)

@@ -264,9 +264,8 @@ int32_t fp8_block_linear(const uint16_t* x_bf16, const uint8_t* w_e4m3, const fl
                          int32_t K, uint16_t* y_bf16, void* ws, size_t ws_bytes, void* stream) {
   (void)ws; (void)ws_bytes;
   if (!x_bf16 || !w_e4m3 || !s || !y_bf16) return W4A8_ERR_NULL;
-  if (M < 1 || M > 16 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return W4A8_ERR_SHAPE;
-  if ((int64_t)N * K >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
-  if ((int64_t)M * K * 2 > 65536) return W4A8_ERR_UNSUPPORTED;   // activation rows staged in 64 KB of LDS
+  if (M < 1 || M > 64 || N < 16 || N % 16 != 0 || K < 128 || K % 128 != 0) return W4A8_ERR_SHAPE;
+  if ((int64_t)N * K >= (int64_t(1) << 40) || (int64_t)M * K >= (int64_t(1) << 30)) return W4A8_ERR_SHAPE;
   if (!aligned16(x_bf16) || !aligned16(w_e4m3) || !aligned16(s) || !aligned16(y_bf16)) return W4A8_ERR_ALIGN;
   launch_fp8_block_linear(x_bf16, w_e4m3, s, M, N, K, y_bf16, as_stream(stream));
   return launch_status();

@@ -144,6 +144,126 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
   *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
 }
 
+// Block-FP8 GEMV past 16 rows or past 64 KB of activations: the chunked staging of
+// fp8_linear_wide_kernel with the activations kept bf16 (16-byte units, so a 64 KB chunk
+// holds CK = 4 / NT blocks of each K-quarter) and the per-128-block scales of this call.
+// Unit (q, cb, j, g, m) = 8 bf16 of row m at K = (q*per + c*CK + cb)*128 + g*32 + j*8, at
+// byte (((((q*CK + cb)*4 + j)*4 + g)*Mp + m) << 4), Mp = 16 * NT.
+template <int RB, int NT>
+__global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_wide_kernel(
+    const uint16_t* __restrict__ x, const uint8_t* __restrict__ w, const float* __restrict__ S, int M, int N, int K,
+    uint16_t* __restrict__ y) {
+  constexpr int kWaves = RB * kBlSplit, Mp = 16 * NT, CK = 4 / NT;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int KB = K >> 7;
+  const int per = (KB + kBlSplit - 1) / kBlSplit;
+  const int chunks = (per + CK - 1) / CK;
+  const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);
+  const bool rb_ok = blockIdx.x * RB + wave / kBlSplit < N / 16;
+  const int part_k = wave % kBlSplit;
+  const int i = lane & 15, g = lane >> 4;
+  const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
+  const float* srow = S + (size_t)((rb * 16) >> 7) * KB;
+  const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
+
+  v4f acc[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
+  uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0;
+  if (kb_begin < kb_end) {
+    q0 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128);
+    q1 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128 + 16);
+  }
+  const int units = kBlSplit * CK * 16 * M;
+  for (int c = 0; c < chunks; ++c) {
+    if (c > 0) lds_barrier();
+    for (int u = tid; u < units; u += kWaves * kWave) {
+      const int m = u % M, r = u / M;
+      const int jg = r & 15, qcb = r >> 4;
+      const int gg = jg >> 2, jj = jg & 3, cb = qcb % CK, q = qcb / CK;
+      const int kb = q * per + c * CK + cb;
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (kb < min(KB, (q + 1) * per) && c * CK + cb < per)
+        v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + kb * 128 + gg * 32 + jj * 8);
+      *reinterpret_cast<uint4*>(lds + (((((q * CK + cb) * 4 + jj) * 4 + gg) * Mp + m) << 4)) = v;
+    }
+    lds_barrier();
+#pragma unroll
+    for (int cb = 0; cb < CK; ++cb) {
+      const int kb = kb_begin + c * CK + cb;
+      if (kb < kb_end) {
+        const uint4 a0 = q0, a1 = q1;
+        if (kb + 1 < kb_end) {
+          q0 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128);
+          q1 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128 + 16);
+        }
+        const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        v4f blk[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) blk[t] = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t d0, d1, d2, d3;
+          e4m3x4_to_bf16x4(cw[2 * j], d0, d1);
+          e4m3x4_to_bf16x4(cw[2 * j + 1], d2, d3);
+          const v8bf a = bf16_operand(d0, d1, d2, d3);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const int m = t * 16 + i;
+            uint4 bv = make_uint4(0u, 0u, 0u, 0u);
+            if (m < M)
+              bv = *reinterpret_cast<const uint4*>(lds + (((((part_k * CK + cb) * 4 + j) * 4 + g) * Mp + m) << 4));
+            blk[t] = mfma_bf16_16x16x32(a, bf16_operand(bv.x, bv.y, bv.z, bv.w), blk[t]);
+          }
+        }
+        const float sc = srow[kb];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          acc[t][0] += sc * blk[t][0]; acc[t][1] += sc * blk[t][1];
+          acc[t][2] += sc * blk[t][2]; acc[t][3] += sc * blk[t][3];
+        }
+      }
+    }
+  }
+  v4f* part = reinterpret_cast<v4f*>(lds);
+  __syncthreads();
+  if (part_k > 0) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) part[((wave - 1) * NT + t) * kWave + lane] = acc[t];
+  }
+  __syncthreads();
+  if (part_k > 0 || !rb_ok) return;
+  const int n = rb * 16 + 4 * g;
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = t * 16 + i;
+    v4f a = acc[t];
+#pragma unroll
+    for (int v = 1; v < kBlSplit; ++v) {
+      const v4f o = part[((wave + v - 1) * NT + t) * kWave + lane];
+      a[0] += o[0]; a[1] += o[1]; a[2] += o[2]; a[3] += o[3];
+    }
+    if (m < M) {
+      uint2 o;
+      o.x = f32_to_bf16_bits(a[0]) | f32_to_bf16_bits(a[1]) << 16;
+      o.y = f32_to_bf16_bits(a[2]) | f32_to_bf16_bits(a[3]) << 16;
+      *reinterpret_cast<uint2*>(y + (size_t)m * N + n) = o;
+    }
+  }
+}
+
+template <int NT>
+static void launch_blw(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K, uint16_t* y,
+                       hipStream_t st) {
+  constexpr int RB = 2;
+  const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
+  const size_t lds = std::max((size_t)kBlSplit * (4 / NT) * 128 * 16 * NT * 2,
+                              (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f));
+  hipLaunchKernelGGL((fp8_block_linear_wide_kernel<RB, NT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, x, w,
+                     s, M, N, K, y);
+}
+
 template <int RB>
 static void launch_bl(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K, uint16_t* y,
                       hipStream_t st) {
@@ -163,9 +283,17 @@ void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s
 #ifndef W4A8_BL_RB_LARGE_M
 #define W4A8_BL_RB_LARGE_M 4
 #endif
-  // fewer row blocks per workgroup while staging x costs little, more as M grows
-  if (M <= 2) launch_bl<W4A8_BL_RB_SMALL_M>(x, w, s, M, N, K, y, st);
-  else launch_bl<W4A8_BL_RB_LARGE_M>(x, w, s, M, N, K, y, st);
+  // fewer row blocks per workgroup while staging x costs little, more as M grows; past 16
+  // rows or 64 KB of bf16 activations, the chunked kernel
+  if (M > 16 || (int64_t)M * K * 2 > 65536) {
+    if (M <= 16) launch_blw<1>(x, w, s, M, N, K, y, st);
+    else if (M <= 32) launch_blw<2>(x, w, s, M, N, K, y, st);
+    else launch_blw<4>(x, w, s, M, N, K, y, st);
+  } else if (M <= 2) {
+    launch_bl<W4A8_BL_RB_SMALL_M>(x, w, s, M, N, K, y, st);
+  } else {
+    launch_bl<W4A8_BL_RB_LARGE_M>(x, w, s, M, N, K, y, st);
+  }
 }
 
 // ---------------------------------------------------------------- per-tensor FP8 linear
