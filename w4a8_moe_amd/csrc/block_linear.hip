@@ -256,7 +256,7 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_wide_k
 template <int NT>
 static void launch_blw(const uint16_t* x, const uint8_t* w, const float* s, int M, int N, int K, uint16_t* y,
                        hipStream_t st) {
-  constexpr int RB = 2;
+  constexpr int RB = 4;   // four row blocks share one staging of x (2 measured 15-25% slower)
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
   const size_t lds = std::max((size_t)kBlSplit * (4 / NT) * 128 * 16 * NT * 2,
                               (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f));
@@ -498,7 +498,7 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
 template <int NT>
 static void launch_flw(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
                        hipStream_t st) {
-  constexpr int RB = 2;
+  constexpr int RB = 4;   // four row blocks share one staging of x (2 measured 15-25% slower)
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
   const size_t lds = std::max((size_t)kBlSplit * (8 / NT) * 128 * 16 * NT,
                               (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f));
