@@ -27,6 +27,8 @@ Each function names the passage of the source pages it follows:
 * the per-tensor FP8 dense linear (``fp8_linear``) follows page A's ``quant_method``
   "fp8" with static activations (everything but the router gates and ``lm_head``) and
   page B's tensor-wise FP8 quantization.
+* the FP8 KV cache store (``kv_cache_store``) follows page A's ``kv_cache_scheme``
+  static, ``kv_cache_group`` (k_proj, v_proj) and ``min_kv_scale`` 1.0.
 
 Where the pages leave a step open, the reading taken is stated at the function.
 Parity pins for every function live in ``tests/test_oracle_*.py``.
@@ -41,6 +43,7 @@ from .moe import (ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH, activation, act_lipschi
                   moe_error_bound)
 from .block_fp8 import fp8_block_quantize, fp8_block_linear, fp8_block_linear_bruteforce
 from .fp8_linear import fp8_tensor_quantize, fp8_quantize_activations, fp8_linear, fp8_linear_bruteforce
+from .kv_cache import MIN_KV_SCALE, kv_scale, kv_cache_store
 
 __all__ = [
     "E4M3_MAX", "e4m3_decode", "e4m3_encode", "e4m3_table",
@@ -52,4 +55,5 @@ __all__ = [
     "moe_error_bound", "expert_gate_up", "expert_down",
     "fp8_block_quantize", "fp8_block_linear", "fp8_block_linear_bruteforce",
     "fp8_tensor_quantize", "fp8_quantize_activations", "fp8_linear", "fp8_linear_bruteforce",
+    "MIN_KV_SCALE", "kv_scale", "kv_cache_store",
 ]
