@@ -6,7 +6,8 @@
  *  - page "ROCm: enable trillion-parameter MoE models with INT4-FP8 single node"
  *    (sglang pull request 4152): "INT4 MoE weights, FP8 compute"; the Grok-1
  *    W4A8KV8 config.json quantization_config: quant_method fp8, int4_experts {bits 4,
- *    sym true, group column}, activation_scheme static, export pack_method reorder; routing
+ *    sym true, group column}, activation_scheme static, kv_cache_scheme static, export
+ *    pack_method reorder, kv_cache_group and min_kv_scale; routing
  *    num_local_experts 8, num_experts_per_tok 2, the router gate left unquantized
  *    (ignored_layers).
  *  - page "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm" (sglang
@@ -281,6 +282,22 @@ int32_t fp8_tensor_quant(const uint16_t* w_bf16, int64_t n, uint8_t* w_e4m3, flo
 int32_t fp8_linear_w8a8(const uint16_t* x_bf16, float s_x, const uint8_t* w_e4m3, float s_w,
                         int32_t M, int32_t N, int32_t K, uint16_t* y_bf16,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * fp8_kv_cache_store -- the FP8 KV cache with static scales (page "ROCm: enable
+ *   trillion-parameter MoE models with INT4-FP8 single node": kv_cache_scheme static,
+ *   export kv_cache_group ["*k_proj", "*v_proj"], min_kv_scale 1.0): each token's key and
+ *   value rows quantized with their group's static scale, e4m3(fp32(v / s)) (nearest even,
+ *   saturating), written to row slots[t] of the group's cache.
+ *   k_bf16, v_bf16 [T][D] (D = key/value heads x head dim, D % 8 == 0), slots [T] int32
+ *   (a slot outside [0, num_slots) marks a token that is not stored), s_k, s_v > 0 (the
+ *   caller applies the min_kv_scale floor), k_cache, v_cache [num_slots][D] E4M3 (in/out:
+ *   rows not written keep their bytes). Slots of one call must be distinct.
+ *   Workspace: none.
+ */
+int32_t fp8_kv_cache_store(const uint16_t* k_bf16, const uint16_t* v_bf16, const int32_t* slots,
+                           int32_t T, int32_t D, float s_k, float s_v,
+                           uint8_t* k_cache, uint8_t* v_cache, int32_t num_slots, void* stream);
 
 /* Workspace size in bytes of one call (0 when none is needed); 0 also for bad args. */
 size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t I_or_K, int32_t E);

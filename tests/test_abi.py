@@ -19,6 +19,7 @@ def test_exports_every_declared_function(L):
     names = W.header_functions()
     assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_route_sort_quant", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
                           "fp8_block_quant", "fp8_block_linear", "fp8_tensor_quant", "fp8_linear_w8a8",
+                          "fp8_kv_cache_store",
                           "w4a8_workspace_bytes", "w4a8_status_str", "w4a8_moe_kernel"}
     for n in names:
         assert hasattr(L, n), n
@@ -198,3 +199,16 @@ def test_fp8_linear_w8a8_validation(L):
     assert call(w=None) == W.ERR_NULL
     assert call(y=U) == W.ERR_ALIGN
     assert call(x=U) == W.ERR_ALIGN
+
+
+def test_kv_cache_store_validation(L):
+    def call(T=4, D=128, s_k=1.0, s_v=1.0, k=A, v=A, slots=A, kc=A, vc=A, S=16):
+        return L.fp8_kv_cache_store(k, v, slots, T, D, s_k, s_v, kc, vc, S, None)
+    assert call(T=-1) == W.ERR_SHAPE
+    assert call(D=12) == W.ERR_SHAPE
+    assert call(S=0) == W.ERR_SHAPE
+    assert call(s_k=0.0) == W.ERR_ARG
+    assert call(s_v=float("inf")) == W.ERR_ARG
+    assert call(T=0, k=None) == W.OK                           # nothing to store
+    assert call(slots=None) == W.ERR_NULL
+    assert call(vc=U) == W.ERR_ALIGN

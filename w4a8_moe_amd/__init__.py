@@ -45,6 +45,7 @@ _SIGNATURES = {
     "fp8_block_linear": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "fp8_tensor_quant": (_I32, [_P, _I64, _P, _P, _P, _SZ, _P]),
     "fp8_linear_w8a8": (_I32, [_P, _F32, _P, _F32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "fp8_kv_cache_store": (_I32, [_P, _P, _P, _I32, _I32, _F32, _F32, _P, _P, _I32, _P]),
     "w4a8_workspace_bytes": (_SZ, [_I32, _I32, _I32, _I32, _I32]),
     "w4a8_status_str": (ctypes.c_char_p, [_I32]),
     "w4a8_moe_kernel": (_I32, [_I32]),
@@ -338,6 +339,22 @@ def fp8_linear_w8a8(x, s_x, w, s_w, out=None, ws=None):
                                                     _ptr(ws) if nws > 0 else None, ws.numel() if nws > 0 else 0,
                                                     _stream(x.device)))
     return y
+
+
+def fp8_kv_cache_store(k, v, slots, s_k, s_v, k_cache, v_cache):
+    """bf16 k, v [T, D], int32 slots [T], static scales (host floats), uint8 E4M3 caches
+    [num_slots, D] updated in place: row slots[t] gets e4m3(k[t] / s_k), e4m3(v[t] / s_v)."""
+    torch = _torch()
+    T, D = k.shape
+    S = k_cache.shape[0]
+    _need(k, torch.bfloat16, (T, D), "k")
+    _need(v, torch.bfloat16, (T, D), "v")
+    _need(slots, torch.int32, (T,), "slots")
+    _need(k_cache, torch.uint8, (S, D), "k_cache")
+    _need(v_cache, torch.uint8, (S, D), "v_cache")
+    _check("fp8_kv_cache_store", lib().fp8_kv_cache_store(_ptr(k), _ptr(v), _ptr(slots), T, D, float(s_k), float(s_v),
+                                                          _ptr(k_cache), _ptr(v_cache), S, _stream(k.device)))
+    return k_cache, v_cache
 
 
 def moe_layer(x, s_x, logits, w13, s_w13, w2, s_w2, act, s_a, out_dtype="bf16"):

@@ -298,4 +298,19 @@ int32_t fp8_linear_w8a8(const uint16_t* x_bf16, float s_x, const uint8_t* w_e4m3
   return launch_status();
 }
 
+int32_t fp8_kv_cache_store(const uint16_t* k_bf16, const uint16_t* v_bf16, const int32_t* slots, int32_t T,
+                           int32_t D, float s_k, float s_v, uint8_t* k_cache, uint8_t* v_cache, int32_t num_slots,
+                           void* stream) {
+  if (T < 0 || D < 8 || D % 8 != 0 || num_slots < 1 || (int64_t)num_slots * D >= (int64_t(1) << 40))
+    return W4A8_ERR_SHAPE;
+  if ((int64_t)T * D >= (int64_t(1) << 40) || T > 0x7FFFFFFF / 2) return W4A8_ERR_SHAPE;
+  if (!good_scale(s_k) || !good_scale(s_v)) return W4A8_ERR_ARG;
+  if (T == 0) return W4A8_OK;
+  if (!k_bf16 || !v_bf16 || !slots || !k_cache || !v_cache) return W4A8_ERR_NULL;
+  if (!aligned16(k_bf16) || !aligned16(v_bf16) || !aligned16(slots) || !aligned16(k_cache) || !aligned16(v_cache))
+    return W4A8_ERR_ALIGN;
+  launch_kv_cache_store(k_bf16, v_bf16, slots, T, D, s_k, s_v, k_cache, v_cache, num_slots, as_stream(stream));
+  return launch_status();
+}
+
 }  // extern "C"

@@ -20,6 +20,9 @@ void launch_w4_tile(const int32_t* packed, int64_t E, int N, int K, int32_t* til
 void launch_fp8_quant(const uint16_t* x, int64_t n, float s, uint8_t* out, hipStream_t st);
 int fp8_quant_blocks(int64_t n);      // 256-thread workgroups of one quantization launch
 void launch_fp8_block_quant(const uint16_t* w, int N, int K, uint8_t* q, float* S, hipStream_t st);
+// KV cache store: rows of k and v [T][D] to E4M3 with their scales, into rows slots[t]
+void launch_kv_cache_store(const uint16_t* k, const uint16_t* v, const int32_t* slots, int T, int D, float s_k,
+                           float s_v, uint8_t* k_cache, uint8_t* v_cache, int num_slots, hipStream_t st);
 constexpr int kTensorQuantParts = 1024;   // most partial maxima of one fp8_tensor_quant
 // two launches: partial maxima into partial[kTensorQuantParts], then scale + codes
 void launch_fp8_tensor_quant(const uint16_t* w, int64_t n, uint8_t* q, float* s, uint32_t* partial,

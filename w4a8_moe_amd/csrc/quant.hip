@@ -8,6 +8,8 @@
 //    activation_scheme static).
 //  * fp8_block_quant: 128x128 block-scaled E4M3 weights (FP8_PB_WO layout of the page
 //    "qwen4_exp: serve the block-FP8 dense projections natively (+25% decode)").
+//  * fp8_kv_cache_store: key and value rows to E4M3 with their static group scales, into
+//    cache slots (kv_cache_scheme static, kv_cache_group k_proj / v_proj of the first page).
 //  * fp8_tensor_quant: tensor-wise E4M3 weights, one scale max|w| / 448 for the tensor
 //    (the dense projections of the first page's quant_method "fp8"; tensor-wise FP8
 //    quantization in the Highlights of the second).
@@ -222,6 +224,34 @@ void launch_fp8_tensor_quant(const uint16_t* w, int64_t n, uint8_t* q, float* s,
   hipLaunchKernelGGL(tensor_amax_kernel, dim3((unsigned)parts), dim3(kTqThreads), 0, st, w, n, partial);
   hipLaunchKernelGGL(tensor_quant_kernel, dim3((unsigned)parts), dim3(kTqThreads), 0, st, w, n, partial, parts, q,
                      s);
+}
+
+// ---------------------------------------------------------------- fp8_kv_cache_store
+// Workgroup (token t, group k or v): 8 elements per thread and round, quantized with the
+// group's scale (correctly rounded quotient, nearest even, saturated) and written to row
+// slots[t] of the group's cache. A slot outside [0, num_slots) stores nothing.
+__global__ __launch_bounds__(256) void kv_cache_store_kernel(const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             const int32_t* __restrict__ slots, int D, float s_k,
+                                                             float s_v, uint8_t* __restrict__ k_cache,
+                                                             uint8_t* __restrict__ v_cache, int num_slots) {
+  const int t = blockIdx.x;
+  const int slot = slots[t];
+  if (slot < 0 || slot >= num_slots) return;
+  const bool is_v = blockIdx.y == 1;
+  const uint4* src = reinterpret_cast<const uint4*>((is_v ? v : k) + (size_t)t * D);
+  uint2* dst = reinterpret_cast<uint2*>((is_v ? v_cache : k_cache) + (size_t)slot * D);
+  const float s = is_v ? s_v : s_k;
+  for (int i = threadIdx.x; i < D / 8; i += blockDim.x) {
+    const uint4 q = src[i];
+    dst[i] = make_uint2(quant4_e4m3(q.x, q.y, s), quant4_e4m3(q.z, q.w, s));
+  }
+}
+
+void launch_kv_cache_store(const uint16_t* k, const uint16_t* v, const int32_t* slots, int T, int D, float s_k,
+                           float s_v, uint8_t* k_cache, uint8_t* v_cache, int num_slots, hipStream_t st) {
+  hipLaunchKernelGGL(kv_cache_store_kernel, dim3((unsigned)T, 2), dim3(std::min(256, std::max(64, D / 8))), 0, st, k,
+                     v, slots, D, s_k, s_v, k_cache, v_cache, num_slots);
 }
 
 }  // namespace w4a8
