@@ -191,6 +191,28 @@ def bench_fp8_linear(torch, W, dev, reps=16, iters=50):
     return out
 
 
+def bench_kv_store(torch, W, dev, T=32, D=1024, slots_total=65536, iters=100):
+    """FP8 KV cache store at the Grok-1 decode step (32 tokens, 8 key/value heads of 128),
+    into a 64K-slot cache; the scales are the min_kv_scale floor (1.0)."""
+    rng = np.random.default_rng(9)
+    k = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    v = torch.from_numpy(rng.standard_normal((T, D)).astype(np.float32)).to(dev).to(torch.bfloat16)
+    slots = torch.from_numpy(rng.choice(slots_total, T, replace=False).astype(np.int32)).to(dev)
+    kc = torch.zeros((slots_total, D), dtype=torch.uint8, device=dev)
+    vc = torch.zeros_like(kc)
+    for _ in range(5):
+        W.fp8_kv_cache_store(k, v, slots, 1.0, 1.0, kc, vc)
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(st)
+    for _ in range(iters):
+        W.fp8_kv_cache_store(k, v, slots, 1.0, 1.0, kc, vc)
+    ev[1].record(st)
+    torch.cuda.synchronize()
+    us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+    return {"us": round(us, 3), "tokens": T, "row_elements": D}
+
+
 def copy_bandwidth(torch, dev, nbytes=1 << 30, iters=10):
     """A plain device-to-device copy of 1 GiB (read + write bytes per second): the
     measured reference beside the 8 TB/s published peak."""
@@ -397,6 +419,7 @@ def main():
     if not args.no_block_gemv:
         result["block_fp8_gemv"] = bench_block_gemv(torch, W, dev)
         result["fp8_linear_w8a8"] = bench_fp8_linear(torch, W, dev)
+        result["fp8_kv_cache_store"] = bench_kv_store(torch, W, dev)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, *static_scales(cfg.name), ids)
     print(json.dumps(result), flush=True)
