@@ -144,9 +144,13 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
   *reinterpret_cast<uint2*>(y + (size_t)i * N + n) = o;
 }
 
-// Block-FP8 GEMV past 16 rows or past 64 KB of activations: the chunked staging of
-// fp8_linear_wide_kernel with the activations kept bf16 (16-byte units, so a 64 KB chunk
-// holds CK = 4 / NT blocks of each K-quarter) and the per-128-block scales of this call.
+// Block-FP8 GEMV past 16 rows or past 64 KB of activations: the mapping of the whole-x
+// kernel with NT 16-column tiles of rows per weight block, the bf16 activations staged in
+// LDS chunk by chunk: all waves walk their K-quarters in step, CK = 4 / NT 128-K blocks at
+// a time, and a chunk holds those blocks of all four quarters for all rows (64 KB), a
+// barrier per chunk; the per-128-block scales applied per block. (Reading the activations
+// straight from L2 instead, as the per-tensor FP8 linear does with its 1-byte codes,
+// measured slower here: 27.7 vs 18.0 us at 32 rows of [16384, 2560], twice the bytes.)
 // Unit (q, cb, j, g, m) = 8 bf16 of row m at K = (q*per + c*CK + cb)*128 + g*32 + j*8, at
 // byte (((((q*CK + cb)*4 + j)*4 + g)*Mp + m) << 4), Mp = 16 * NT.
 template <int RB, int NT>
@@ -391,85 +395,83 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
 }
 
 // Up to 64 rows, any K: the same mapping (four waves per 16-row block, one K-quarter each),
-// with NT 16-column tiles of rows per weight block, and the activation codes staged chunk
-// by chunk: all waves walk their quarters in step, CK 128-K blocks at a time, and a chunk
-// holds those blocks of all four quarters for all rows (64 KB: CK = 8 / NT, so 8, 4 or 2).
-// Unit (q, cb, j, g, m) = 8 codes of row m at K = (q*per + c*CK + cb)*128 + g*32 + j*8, at
-// byte (((((q*CK + cb)*4 + j)*4 + g)*Mp + m) << 3), Mp = 16 * NT.
+// with NT 16-column tiles of rows per weight block, and the B operands (the activation
+// codes, M x K bytes, resident in L2) read by each lane straight from global memory one
+// 128-K block ahead, with no LDS staging and no barrier in the k-loop. Staging them in LDS
+// chunk by chunk instead (every workgroup restaging all of x behind a barrier per chunk)
+// measured 31.4 us against 21.9 us at 32 rows of the Grok-1 q|k|v projection.
 template <int RB, int NT>
 __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
     uint16_t* __restrict__ y) {
-  constexpr int kWaves = RB * kBlSplit, Mp = 16 * NT, kChunkKB = 8 / NT;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+  const int lane = lane_id(), wave = wave_id();
   const int KB = K >> 7;
-  const int per = (KB + kBlSplit - 1) / kBlSplit;           // 128-K blocks per quarter (the last may be short)
-  const int chunks = (per + kChunkKB - 1) / kChunkKB;
+  const int per = (KB + kBlSplit - 1) / kBlSplit;
   const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);
   const bool rb_ok = blockIdx.x * RB + wave / kBlSplit < N / 16;
   const int part_k = wave % kBlSplit;
   const int i = lane & 15, g = lane >> 4;
   const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
   const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
-
+  const uint8_t* xp[NT];
+  bool mok[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = t * 16 + i;
+    mok[t] = m < M;
+    xp[t] = xq + (size_t)(mok[t] ? m : 0) * K + g * 32;
+  }
   v4f acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0;
+  uint4 b0[NT], b1[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) { b0[t] = q0; b1[t] = q0; }
   if (kb_begin < kb_end) {
     q0 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128);
     q1 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128 + 16);
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+      if (mok[t]) {
+        b0[t] = *reinterpret_cast<const uint4*>(xp[t] + kb_begin * 128);
+        b1[t] = *reinterpret_cast<const uint4*>(xp[t] + kb_begin * 128 + 16);
+      }
   }
-  const int units = kBlSplit * kChunkKB * 16 * M;            // 8-code units of one chunk
-  for (int c = 0; c < chunks; ++c) {
-    if (c > 0) lds_barrier();                                // every wave is done with chunk c - 1
-    for (int u = tid; u < units; u += kWaves * kWave) {
-      const int m = u % M, r = u / M;                        // r = ((q*kChunkKB + cb)*16 + g*4 + j)
-      const int jg = r & 15, qcb = r >> 4;
-      const int gg = jg >> 2, jj = jg & 3, cb = qcb % kChunkKB, q = qcb / kChunkKB;
-      const int kb = q * per + c * kChunkKB + cb;
-      uint2 v = make_uint2(0u, 0u);
-      if (kb < min(KB, (q + 1) * per) && c * kChunkKB + cb < per)
-        v = *reinterpret_cast<const uint2*>(xq + (size_t)m * K + kb * 128 + gg * 32 + jj * 8);
-      *reinterpret_cast<uint2*>(lds + (((((q * kChunkKB + cb) * 4 + jj) * 4 + gg) * Mp + m) << 3)) = v;
+  for (int kb = kb_begin; kb < kb_end; ++kb) {
+    const uint4 a0 = q0, a1 = q1;
+    uint4 c0[NT], c1[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) { c0[t] = b0[t]; c1[t] = b1[t]; }
+    if (kb + 1 < kb_end) {
+      q0 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128);
+      q1 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128 + 16);
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        if (mok[t]) {
+          b0[t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + 1) * 128);
+          b1[t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + 1) * 128 + 16);
+        }
     }
-    lds_barrier();
+    const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-    for (int cb = 0; cb < kChunkKB; ++cb) {
-      const int kb = kb_begin + c * kChunkKB + cb;
-      if (kb < kb_end) {
-        const uint4 a0 = q0, a1 = q1;
-        if (kb + 1 < kb_end) {
-          q0 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128);
-          q1 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128 + 16);
-        }
-        const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+    for (int j = 0; j < 4; ++j) {
+      uint32_t d0, d1, d2, d3;
+      e4m3x4_to_bf16x4(cw[2 * j], d0, d1);
+      e4m3x4_to_bf16x4(cw[2 * j + 1], d2, d3);
+      const v8bf a = bf16_operand(d0, d1, d2, d3);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t d0, d1, d2, d3;
-          e4m3x4_to_bf16x4(cw[2 * j], d0, d1);
-          e4m3x4_to_bf16x4(cw[2 * j + 1], d2, d3);
-          const v8bf a = bf16_operand(d0, d1, d2, d3);
-#pragma unroll
-          for (int t = 0; t < NT; ++t) {
-            const int m = t * 16 + i;
-            uint2 bx = make_uint2(0u, 0u);
-            if (m < M)
-              bx = *reinterpret_cast<const uint2*>(
-                  lds + (((((part_k * kChunkKB + cb) * 4 + j) * 4 + g) * Mp + m) << 3));
-            uint32_t e0, e1, e2, e3;
-            e4m3x4_to_bf16x4(bx.x, e0, e1);
-            e4m3x4_to_bf16x4(bx.y, e2, e3);
-            acc[t] = mfma_bf16_16x16x32(a, bf16_operand(e0, e1, e2, e3), acc[t]);
-          }
-        }
+      for (int t = 0; t < NT; ++t) {
+        const uint32_t bw[8] = {c0[t].x, c0[t].y, c0[t].z, c0[t].w, c1[t].x, c1[t].y, c1[t].z, c1[t].w};
+        uint32_t e0, e1, e2, e3;
+        e4m3x4_to_bf16x4(bw[2 * j], e0, e1);
+        e4m3x4_to_bf16x4(bw[2 * j + 1], e2, e3);
+        acc[t] = mfma_bf16_16x16x32(a, bf16_operand(e0, e1, e2, e3), acc[t]);
       }
     }
   }
-  // partial sums of a row block's waves, added in K-part order over the staged codes
   v4f* part = reinterpret_cast<v4f*>(lds);
-  __syncthreads();
   if (part_k > 0) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) part[((wave - 1) * NT + t) * kWave + lane] = acc[t];
@@ -498,10 +500,9 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
 template <int NT>
 static void launch_flw(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
                        hipStream_t st) {
-  constexpr int RB = 4;   // four row blocks share one staging of x (2 measured 15-25% slower)
+  constexpr int RB = 1;   // one row block per workgroup (2 measured the same)
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
-  const size_t lds = std::max((size_t)kBlSplit * (8 / NT) * 128 * 16 * NT,
-                              (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f));
+  const size_t lds = (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f);   // the partial sums
   hipLaunchKernelGGL((fp8_linear_wide_kernel<RB, NT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w,
                      scale, M, N, K, y);
 }
