@@ -22,12 +22,13 @@
 // block, W4A8_BL_DEPTH blocks in flight, W4A8_BL_RB_SMALL_M / W4A8_BL_RB_LARGE_M row
 // blocks per workgroup for M <= 2 / M > 2.
 //
-// The per-tensor FP8 linear (fp8_linear_kernel, the dense projections of the W4A8 model:
-// quant_method "fp8" with static activations on the page "ROCm: enable trillion-parameter
-// MoE models with INT4-FP8 single node") has the same mapping; its activations are
-// quantized with their static scale (inside the kernel for M <= 2), staged as E4M3 bytes
-// (M x K in LDS, half the bf16 size), both operands are widened to bf16 in registers
-// (exact), and the one scale s_x * s_w multiplies the sum.
+// The per-tensor FP8 linear (the dense projections of the W4A8 model: quant_method "fp8"
+// with static activations on the page "ROCm: enable trillion-parameter MoE models with
+// INT4-FP8 single node") has the same mapping; its activations are quantized with their
+// static scale, both operands are widened to bf16 in registers (exact), and the one scale
+// s_x * s_w multiplies the sum. Up to 2 rows fp8_linear_kernel quantizes the activations
+// itself and stages their codes in LDS (one launch); above, fp8_linear_wide_kernel reads
+// the codes, quantized once into the workspace, straight from L2.
 #include <algorithm>
 
 #include "common.h"
@@ -304,14 +305,13 @@ void launch_fp8_block_linear(const uint16_t* x, const uint8_t* w, const float* s
 // y[m][n] = bf16( scale * sum_k dec(xq[m][k]) * dec(W[n][k]) ), scale = s_x * s_w.
 // Staged unit (kb, j, g, m) = 8 codes of x[m][kb*128 + g*32 + j*8 .. +8] at byte
 // ((((kb*4 + j)*4 + g)*M + m) << 3): lane (m, g) of MFMA j reads 8 contiguous bytes.
-// With QUANT, every workgroup quantizes the M x K activations itself while staging them
-// (the arithmetic of fp8_quant_static: correctly rounded x / s_x, nearest even,
-// saturated), and the call is one launch: the path for M <= 2. Without QUANT the kernel
-// stages codes quantized beforehand (xq).
-template <int RB, bool QUANT>   // 16-row blocks per workgroup; quantize x in the kernel
+// Every workgroup quantizes the M x K activations itself while staging them (the
+// arithmetic of fp8_quant_static: correctly rounded x / s_x, nearest even, saturated), and
+// the call is one launch: the path for M <= 2 (a few KB of activations).
+template <int RB>   // 16-row blocks per workgroup
 __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
-    const uint16_t* __restrict__ x, float s_x, const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w,
-    float scale, int M, int N, int K, uint16_t* __restrict__ y) {
+    const uint16_t* __restrict__ x, float s_x, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
+    uint16_t* __restrict__ y) {
   constexpr int kWaves = RB * kBlSplit;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
@@ -321,14 +321,9 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
     const int m = u / (K >> 3), c8 = u - m * (K >> 3);
     const int kb = c8 >> 4, within = c8 & 15;
     const int g = within >> 2, j = within & 3;
-    uint2 codes;
-    if (QUANT) {
-      const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + c8 * 8);
-      codes = make_uint2(quant4_e4m3(v.x, v.y, s_x), quant4_e4m3(v.z, v.w, s_x));
-    } else {
-      codes = *reinterpret_cast<const uint2*>(xq + (size_t)m * K + c8 * 8);
-    }
-    *reinterpret_cast<uint2*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 3)) = codes;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + c8 * 8);
+    *reinterpret_cast<uint2*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 3)) =
+        make_uint2(quant4_e4m3(v.x, v.y, s_x), quant4_e4m3(v.z, v.w, s_x));
   }
   __syncthreads();
   const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);
@@ -507,13 +502,13 @@ static void launch_flw(const uint8_t* xq, const uint8_t* w, float scale, int M, 
                      scale, M, N, K, y);
 }
 
-template <int RB, bool QUANT>
-static void launch_fl(const uint16_t* x, float s_x, const uint8_t* xq, const uint8_t* w, float scale, int M, int N,
-                      int K, uint16_t* y, hipStream_t st) {
+template <int RB>
+static void launch_fl(const uint16_t* x, float s_x, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
+                      hipStream_t st) {
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
   const size_t lds = std::max((size_t)M * K, (size_t)(RB * kBlSplit - 1) * kWave * sizeof(v4f));
-  hipLaunchKernelGGL((fp8_linear_kernel<RB, QUANT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, x, s_x, xq,
-                     w, scale, M, N, K, y);
+  hipLaunchKernelGGL((fp8_linear_kernel<RB>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, x, s_x, w, scale, M,
+                     N, K, y);
 }
 
 bool fp8_linear_quant_inside(int M) { return M <= 2; }
@@ -524,7 +519,7 @@ static bool fp8_linear_whole_x(int M, int K) { return M <= 16 && (int64_t)M * K 
 void launch_fp8_linear(const uint16_t* x, float s_x, uint8_t* xq, const uint8_t* w, float scale, int M, int N,
                        int K, uint16_t* y, hipStream_t st) {
   if (fp8_linear_quant_inside(M) && fp8_linear_whole_x(M, K)) {
-    launch_fl<W4A8_BL_RB_SMALL_M, true>(x, s_x, nullptr, w, scale, M, N, K, y, st);
+    launch_fl<W4A8_BL_RB_SMALL_M>(x, s_x, w, scale, M, N, K, y, st);
     return;
   }
   // the codes quantized once into the workspace, then B read from L2 by every lane (for
