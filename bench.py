@@ -116,8 +116,14 @@ def cpu_baseline(cfg, s_x, s_a, ids, max_tokens=32):
     pairs = [tuple(sorted(map(int, r))) for r in ids]
     best = max(set(pairs), key=pairs.count)
     toks = np.array([t for t, p in enumerate(pairs) if p == best], dtype=np.int64)[:max_tokens]
-    packed13 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w13", e)) for e in best}
-    packed2 = {e: oracle.w4_pack(synth.moe_expert_weights(cfg, "w2", e)) for e in best}
+    w13 = {e: synth.moe_expert_weights(cfg, "w13", e) for e in best}
+    w2 = {e: synth.moe_expert_weights(cfg, "w2", e) for e in best}
+    t0 = time.perf_counter()                                   # the oracle's w4_pack, beside the GPU's
+    packed13 = {e: oracle.w4_pack(w13[e]) for e in best}
+    packed2 = {e: oracle.w4_pack(w2[e]) for e in best}
+    pack_s = time.perf_counter() - t0
+    pack_n = sum(w13[e].size + w2[e].size for e in best)
+    del w13, w2
     # the same forward repeated until about 10 s of host time (at most 8 runs)
     runs, dt = 0, 0.0
     while runs < 8 and dt < 10.0:
@@ -126,7 +132,9 @@ def cpu_baseline(cfg, s_x, s_a, ids, max_tokens=32):
                            tokens=toks, E=cfg.E)
         dt += time.perf_counter() - t0
         runs += 1
-    return {"value": float(runs * len(toks) / dt), "unit": "tokens/s",
+    return {"oracle_w4_pack": {"weights": int(pack_n), "s": round(pack_s, 3),
+                               "GB/s": round(pack_n * 3.5 / pack_s / 1e9, 3)},
+            "value": float(runs * len(toks) / dt), "unit": "tokens/s",
             "cores": int(max(1, blas_threads)), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"{len(toks)} of {cfg.T} tokens (routed to experts {best[0]} and {best[1]}), "
                       f"full oracle forward (fp64, int4 unpack, exact sums), {runs} runs, {dt:.2f} s"}
