@@ -303,7 +303,7 @@ int32_t fp8_kv_cache_store(const uint16_t* k_bf16, const uint16_t* v_bf16, const
                            void* stream) {
   if (T < 0 || D < 8 || D % 8 != 0 || num_slots < 1 || (int64_t)num_slots * D >= (int64_t(1) << 40))
     return W4A8_ERR_SHAPE;
-  if ((int64_t)T * D >= (int64_t(1) << 40) || T > 0x7FFFFFFF / 2) return W4A8_ERR_SHAPE;
+  if ((int64_t)T * D >= (int64_t(1) << 40)) return W4A8_ERR_SHAPE;
   if (!good_scale(s_k) || !good_scale(s_v)) return W4A8_ERR_ARG;
   if (T == 0) return W4A8_OK;
   if (!k_bf16 || !v_bf16 || !slots || !k_cache || !v_cache) return W4A8_ERR_NULL;
