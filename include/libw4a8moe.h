@@ -274,8 +274,9 @@ int32_t fp8_tensor_quant(const uint16_t* w_bf16, int64_t n, uint8_t* w_e4m3, flo
  *   the products are exact and summed in fp32.
  *   x_bf16 [M][K], s_x > 0 (static activation scale, host value), w_e4m3 [N][K] with its
  *   tensor scale s_w >= 0 (host value), y_bf16 [M][N] (out).
- *   Requires 1 <= M <= 64, N % 16 == 0, K % 128 == 0. Up to 16 rows with M * K <= 65536
- *   the codes of x are staged whole in LDS; otherwise they are staged in chunks of K.
+ *   Requires 1 <= M <= 64, N % 16 == 0, K % 128 == 0. Up to 2 rows with M * K <= 65536
+ *   the kernel quantizes x itself and stages the codes in LDS (one launch); otherwise the
+ *   codes are quantized into the workspace first and read from there by the GEMV.
  *   Workspace: w4a8_workspace_bytes(W4A8_OP_FP8_LINEAR, M, N, K, 0) bytes: 0 for M <= 2
  *   with M * K <= 65536 (ws may be NULL), else M * K rounded up to 256 (holds xq).
  */
