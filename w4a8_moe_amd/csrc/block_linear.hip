@@ -151,7 +151,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
 // a time, and a chunk holds those blocks of all four quarters for all rows (64 KB), a
 // barrier per chunk; the per-128-block scales applied per block. (Reading the activations
 // straight from L2 instead, as the per-tensor FP8 linear does with its 1-byte codes,
-// measured slower here: 27.7 vs 18.0 us at 32 rows of [16384, 2560], twice the bytes.)
+// measured slower here: 27.7 vs 18.0 us at 32 rows of [16384, 2560], twice the bytes; with
+// two or three 128-K blocks in flight per lane, 28.0-28.6 vs 17.8 us.)
 // Unit (q, cb, j, g, m) = 8 bf16 of row m at K = (q*per + c*CK + cb)*128 + g*32 + j*8, at
 // byte (((((q*CK + cb)*4 + j)*4 + g)*Mp + m) << 4), Mp = 16 * NT.
 template <int RB, int NT>
@@ -391,11 +392,14 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
 
 // Up to 64 rows, any K: the same mapping (four waves per 16-row block, one K-quarter each),
 // with NT 16-column tiles of rows per weight block, and the B operands (the activation
-// codes, M x K bytes, resident in L2) read by each lane straight from global memory one
-// 128-K block ahead, with no LDS staging and no barrier in the k-loop. Staging them in LDS
-// chunk by chunk instead (every workgroup restaging all of x behind a barrier per chunk)
-// measured 31.4 us against 21.9 us at 32 rows of the Grok-1 q|k|v projection.
-template <int RB, int NT>
+// codes, M x K bytes, resident in L2) read by each lane straight from global memory, D
+// 128-K blocks ahead together with its weights, with no LDS staging and no barrier in the
+// k-loop. Staging them in LDS chunk by chunk instead (every workgroup restaging all of x
+// behind a barrier per chunk) measured 31.4 us against 21.9 us at 32 rows of the Grok-1
+// q|k|v projection. Two blocks ahead measured faster at 8 rows (q|k|v 15.8 -> 15.0 us, o
+// 15.0 -> 14.4 us) and slower at 32 (22.2 -> 23.5 us); three, slower at both.
+// A tile row past M reads row 0 instead: its products reach only output rows not stored.
+template <int RB, int NT, int D>
 __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ w, float scale, int M, int N, int K,
     uint16_t* __restrict__ y) {
@@ -410,59 +414,62 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
   const uint8_t* wp = w + (size_t)(rb * 16 + i) * K + g * 32;
   const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
   const uint8_t* xp[NT];
-  bool mok[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) {
     const int m = t * 16 + i;
-    mok[t] = m < M;
-    xp[t] = xq + (size_t)(mok[t] ? m : 0) * K + g * 32;
+    xp[t] = xq + (size_t)(m < M ? m : 0) * K + g * 32;
   }
   v4f acc[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-  uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0;
-  uint4 b0[NT], b1[NT];
+  uint4 q0[D], q1[D], b0[D][NT], b1[D][NT];     // ring: block kb sits in slot (kb - kb_begin) % D
 #pragma unroll
-  for (int t = 0; t < NT; ++t) { b0[t] = q0; b1[t] = q0; }
-  if (kb_begin < kb_end) {
-    q0 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128);
-    q1 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128 + 16);
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-      if (mok[t]) {
-        b0[t] = *reinterpret_cast<const uint4*>(xp[t] + kb_begin * 128);
-        b1[t] = *reinterpret_cast<const uint4*>(xp[t] + kb_begin * 128 + 16);
-      }
-  }
-  for (int kb = kb_begin; kb < kb_end; ++kb) {
-    const uint4 a0 = q0, a1 = q1;
-    uint4 c0[NT], c1[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) { c0[t] = b0[t]; c1[t] = b1[t]; }
-    if (kb + 1 < kb_end) {
-      q0 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128);
-      q1 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128 + 16);
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-        if (mok[t]) {
-          b0[t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + 1) * 128);
-          b1[t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + 1) * 128 + 16);
-        }
-    }
-    const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t d0, d1, d2, d3;
-      e4m3x4_to_bf16x4(cw[2 * j], d0, d1);
-      e4m3x4_to_bf16x4(cw[2 * j + 1], d2, d3);
-      const v8bf a = bf16_operand(d0, d1, d2, d3);
+  for (int d = 0; d < D; ++d) {
+    const int kb = kb_begin + d;
+    if (kb < kb_end) {
+      q0[d] = *reinterpret_cast<const uint4*>(wp + kb * 128);
+      q1[d] = *reinterpret_cast<const uint4*>(wp + kb * 128 + 16);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
-        const uint32_t bw[8] = {c0[t].x, c0[t].y, c0[t].z, c0[t].w, c1[t].x, c1[t].y, c1[t].z, c1[t].w};
-        uint32_t e0, e1, e2, e3;
-        e4m3x4_to_bf16x4(bw[2 * j], e0, e1);
-        e4m3x4_to_bf16x4(bw[2 * j + 1], e2, e3);
-        acc[t] = mfma_bf16_16x16x32(a, bf16_operand(e0, e1, e2, e3), acc[t]);
+        b0[d][t] = *reinterpret_cast<const uint4*>(xp[t] + kb * 128);
+        b1[d][t] = *reinterpret_cast<const uint4*>(xp[t] + kb * 128 + 16);
+      }
+    }
+  }
+  for (int kb0 = kb_begin; kb0 < kb_end; kb0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kb = kb0 + d;
+      if (kb < kb_end) {
+        const uint4 a0 = q0[d], a1 = q1[d];
+        uint4 c0[NT], c1[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t) { c0[t] = b0[d][t]; c1[t] = b1[d][t]; }
+        if (kb + D < kb_end) {
+          q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + D) * 128);
+          q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + D) * 128 + 16);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            b0[d][t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + D) * 128);
+            b1[d][t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + D) * 128 + 16);
+          }
+        }
+        const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          uint32_t d0, d1, d2, d3;
+          e4m3x4_to_bf16x4(cw[2 * j], d0, d1);
+          e4m3x4_to_bf16x4(cw[2 * j + 1], d2, d3);
+          const v8bf a = bf16_operand(d0, d1, d2, d3);
+#pragma unroll
+          for (int t = 0; t < NT; ++t) {
+            const uint32_t bw[8] = {c0[t].x, c0[t].y, c0[t].z, c0[t].w, c1[t].x, c1[t].y, c1[t].z, c1[t].w};
+            uint32_t e0, e1, e2, e3;
+            e4m3x4_to_bf16x4(bw[2 * j], e0, e1);
+            e4m3x4_to_bf16x4(bw[2 * j + 1], e2, e3);
+            acc[t] = mfma_bf16_16x16x32(a, bf16_operand(e0, e1, e2, e3), acc[t]);
+          }
+        }
       }
     }
   }
@@ -492,13 +499,13 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
   }
 }
 
-template <int NT>
+template <int NT, int D>
 static void launch_flw(const uint8_t* xq, const uint8_t* w, float scale, int M, int N, int K, uint16_t* y,
                        hipStream_t st) {
-  constexpr int RB = 1;   // one row block per workgroup (2 measured the same)
+  constexpr int RB = 1;   // one row block per workgroup (2 measured the same, 4 slower)
   const unsigned grid = (unsigned)((N / 16 + RB - 1) / RB);
   const size_t lds = (size_t)(RB * kBlSplit - 1) * NT * kWave * sizeof(v4f);   // the partial sums
-  hipLaunchKernelGGL((fp8_linear_wide_kernel<RB, NT>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w,
+  hipLaunchKernelGGL((fp8_linear_wide_kernel<RB, NT, D>), dim3(grid), dim3(RB * kBlSplit * kWave), lds, st, xq, w,
                      scale, M, N, K, y);
 }
 
@@ -526,9 +533,9 @@ void launch_fp8_linear(const uint16_t* x, float s_x, uint8_t* xq, const uint8_t*
   // 3..16 rows this measured faster than staging the codes in LDS: 8 rows of q|k|v 19.2 ->
   // 15.7 us, of o 18.3 -> 14.6 us)
   launch_fp8_quant(x, (int64_t)M * K, s_x, xq, st);
-  if (M <= 16) launch_flw<1>(xq, w, scale, M, N, K, y, st);
-  else if (M <= 32) launch_flw<2>(xq, w, scale, M, N, K, y, st);
-  else launch_flw<4>(xq, w, scale, M, N, K, y, st);
+  if (M <= 16) launch_flw<1, 2>(xq, w, scale, M, N, K, y, st);
+  else if (M <= 32) launch_flw<2, 1>(xq, w, scale, M, N, K, y, st);
+  else launch_flw<4, 1>(xq, w, scale, M, N, K, y, st);
 }
 
 }  // namespace w4a8
