@@ -49,7 +49,10 @@ def test_integer_case_bit_exact():
                                    # activations staged in chunks of K: more than 16 rows (up to 64, ragged
                                    # tiles), or M * K past 64 KB, or a ragged last K-quarter
                                    (32, 1024, 6144), (32, 6144, 768), (64, 512, 2560), (20, 256, 6144),
-                                   (17, 128, 128), (16, 256, 8192), (2, 64, 33024), (48, 96, 1152)])
+                                   (17, 128, 128), (16, 256, 8192), (2, 64, 33024), (48, 96, 1152),
+                                   # two blocks in flight per lane: K-quarters of 2, 2, 1 and 0 blocks, of 4, 4,
+                                   # 4 and 1
+                                   (5, 64, 640), (12, 48, 1664)])
 def test_fp8_linear_parity(M, N, K):
     cfg = synth.custom_block("fl", M=M, N=N, K=K, cfg=93, sub=N)
     w = synth.block_weights(cfg)
