@@ -405,7 +405,7 @@ def measure_layer(torch, W, cfg, steps, warmup):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only (the layer on one GPU's share); "
+        print("bench.py measures the layer on one GPU (one GPU's share of the model); "
               "--gpus above 1 is not supported.", file=sys.stderr)
         sys.exit(2)
     import torch

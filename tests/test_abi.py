@@ -212,3 +212,15 @@ def test_kv_cache_store_validation(L):
     assert call(T=0, k=None) == W.OK                           # nothing to store
     assert call(slots=None) == W.ERR_NULL
     assert call(vc=U) == W.ERR_ALIGN
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py measures one GPU: --gpus 2 exits with status 2 and says so, before touching a GPU."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
