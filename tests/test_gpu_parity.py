@@ -229,6 +229,9 @@ PREFILL_CASES = [
     # 9 of 16 experts empty, several with a single row
     synth.custom_moe("pf_empty_experts", T=130, H=256, I=256, E=16, w_cfg=306, x_cfg=306, expert_bias=True,
                      logit_sigma=0.5),
+    # the largest expert count the calls accept: 600 rows over 256 experts, tiles of one to a few rows
+    synth.custom_moe("pf_max_experts", T=300, H=128, I=128, E=256, w_cfg=308, x_cfg=308, out_f32=False,
+                     logit_sigma=2.0),
 ]
 
 
