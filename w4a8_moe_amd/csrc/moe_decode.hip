@@ -371,6 +371,34 @@ static double round_fill(long units, long slots) {
   return rounds > 0 ? (double)units / (double)(rounds * slots) : 1.0;
 }
 
+// Down projection: split K into slices of at most one E4M3 LDS chunk for 16 rows (4096 K),
+// balanced to whole k-steps (a chunk may end with a partial round), and wmax..4 waves per
+// workgroup (32 channels each): the combination that fills the rounds of workgroup slots
+// best, preferring fewer slices (each adds a partial sum to the combine) and then more
+// waves (more loads in flight). Returns its round fill.
+static double plan_down(MoeGemmParams& p, int wmax, long experts, long slots) {
+  const int step = 128;
+  const int kmax = (kDecodeLds / 16) / (128 * kDepth) * (128 * kDepth);
+  const int first = (p.K + kmax - 1) / kmax;
+  double best = -1.0;
+  for (int ks = first; ks <= 4 * first; ++ks) {
+    const int kslice = ((p.K + ks - 1) / ks + step - 1) / step * step;
+    if ((p.K + kslice - 1) / kslice != ks) continue;        // rounding merged two slices
+    for (int w = wmax; w >= std::min(4, kDecodeWaves); --w) {
+      const int groups = (p.n_out + 32 * w - 1) / (32 * w);
+      const double fill = round_fill((long)groups * ks * experts, slots);
+      if (fill > best + 0.02) {
+        best = fill;
+        p.kslice = kslice;
+        p.ksplit = ks;
+        p.waves = w;
+        p.groups = groups;
+      }
+    }
+  }
+  return best;
+}
+
 void plan_decode(MoeGemmParams& p, bool gateup) {
   // an expert never holds more rows than there are tokens (its two slots differ)
   const int T = p.P / 2;
@@ -399,30 +427,16 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
       }
     }
   } else {
-    // split K: slices of at most one E4M3 LDS chunk for 16 rows (4096 K), balanced to whole
-    // k-steps (a chunk may end with a partial round), and 4..8 waves per workgroup (32
-    // channels each): the combination that fills the rounds of workgroup slots best,
-    // preferring fewer slices (each adds a partial sum to the combine) and then more waves
-    // (more loads in flight)
-    const int step = 128;
-    const int kmax = (kDecodeLds / 16) / (128 * kDepth) * (128 * kDepth);
+    // A grid of several rounds takes at most 6 waves when that fills as well (Grok-1 shape,
+    // 8 slices: 8 waves in 3 rounds 182.6 us, 6 waves in 4 rounds 162.0 us, 4 waves 167.6
+    // us; a single round keeps 8: Mixtral shape 50.0 us, 58.6 with 6).
     const long experts = std::min(p.E, 2 * T);
     const long slots = 2L * device_cus();
-    const int first = (p.K + kmax - 1) / kmax;
-    double best = -1.0;
-    for (int ks = first; ks <= 4 * first; ++ks) {
-      const int kslice = ((p.K + ks - 1) / ks + step - 1) / step * step;
-      if ((p.K + kslice - 1) / kslice != ks) continue;      // rounding merged two slices
-      for (int w = kDecodeWaves; w >= std::min(4, kDecodeWaves); --w) {
-        const int groups = (p.n_out + 32 * w - 1) / (32 * w);
-        const double fill = round_fill((long)groups * ks * experts, slots);
-        if (fill > best + 0.02) {
-          best = fill;
-          p.kslice = kslice;
-          p.ksplit = ks;
-          p.waves = w;
-          p.groups = groups;
-        }
+    const double fill = plan_down(p, kDecodeWaves, experts, slots);
+    if ((long)p.groups * p.ksplit * experts > slots && p.waves > 6) {
+      MoeGemmParams q = p;
+      if (plan_down(q, std::min(6, kDecodeWaves), experts, slots) >= fill - 0.02) {
+        p.kslice = q.kslice; p.ksplit = q.ksplit; p.waves = q.waves; p.groups = q.groups;
       }
     }
   }
