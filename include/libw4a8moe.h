@@ -170,8 +170,8 @@ int32_t moe_route_sort_quant(const float* logits, int32_t T, int32_t E,
 
 /*
  * moe_gemm1_w4a8 -- gate|up grouped GEMM of the routed experts with int4 weights
- * upcast to fp8 in registers, fp8 MFMA with fp32 accumulation, fused gated
- * activation and static fp8 requantization ("INT4 MoE weights, FP8 compute",
+ * upcast in registers, products of E4M3 activations and int4 codes with fp32
+ * accumulation, fused gated activation and static fp8 requantization ("INT4 MoE weights, FP8 compute",
  * page "ROCm: enable ..."; int4 weights upcast to float8 for fp8 math, page
  * "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm").
  *
@@ -187,12 +187,14 @@ int32_t moe_route_sort_quant(const float* logits, int32_t T, int32_t E,
  *              h = s_x * s_w13[e][n] * sum_k x_hat[t][k] * q13[e][n][k]   (t = sorted_pair[r]/2)
  *              a_fp8[r][n] = e4m3(fp32(act(h[n]) * h[I+n]) / s_a)
  *   gateup_dbg [2T][2I] fp32 (out, optional, NULL to skip): h per sorted row
- * Accuracy: up to 64 tokens (w4a8_moe_kernel) the products are exact and added in fp32
- * (each code enters as q + 8; 8 times the fp32 sum of the row of x_hat is taken off after
- * the sum, so h carries about twice the rounding of a plain fp32 sum); above it the fp8 matrix instruction adds each 128-long block of products with
- * about 14 bits below its largest product, so h carries a relative error of about
- * 1e-5 of its row's largest value, and a code of a_fp8 can then sit one step from the
- * one an exact h gives.
+ * Accuracy (both kernels of w4a8_moe_kernel): every product x_hat * q is exact (both are
+ * exact in fp16; the 16-bit matrix instruction forms them) and the sums are fp32, so h
+ * differs from the exact sum by fp32 rounding only (about 1e-7 of its row's largest value).
+ * The requantization decision is taken in double precision, from the same h and with the
+ * activation's textbook formula, for every value within a relative 1e-5 of an E4M3
+ * rounding boundary, and from a fast fp32 activation (relative error about 1e-6) for the
+ * others: a code of a_fp8 is then the one that fp32(act(h[n]) * h[I+n]) / s_a, computed
+ * exactly from the kernel's h, rounds to.
  * Requires H % 128 == 0, I % 128 == 0, 2 <= E <= 256, 0 <= T <= 2^22, 2T*H < 2^31, I*H < 2^31.
  * Workspace: w4a8_workspace_bytes(x_dtype == BF16 ? W4A8_OP_GEMM1_BF16 : W4A8_OP_GEMM1, T, H, I, E).
  */
@@ -204,9 +206,9 @@ int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
- * moe_gemm2_w4a8 -- down projection of the routed experts (int4 weights upcast to
- * fp8, fp8 MFMA, fp32 accumulation) and the deterministic top-2 combine (same
- * passages as moe_gemm1_w4a8).
+ * moe_gemm2_w4a8 -- down projection of the routed experts (int4 weights upcast in
+ * registers, exact products of E4M3 codes and int4 codes, fp32 accumulation) and the
+ * deterministic top-2 combine (same passages as moe_gemm1_w4a8).
  *
  *   a_fp8   [2T][I] e4m3 from moe_gemm1_w4a8 (sorted rows);  s_a its static scale
  *   w2      [E][H/16][I/128][256] int32 from w4_tile (of w4_pack's [E][H][I/8]);
@@ -308,8 +310,9 @@ const char* w4a8_status_str(int32_t status);
 
 /* Which kernel the MoE GEMM calls use for T tokens (T >= 0): W4A8_KERNEL_STREAM, the
  * weight-streaming kernel for few tokens per expert (bound by HBM), or
- * W4A8_KERNEL_TILED, the 256 x 256 tiled kernel for many tokens per expert (bound by
- * the fp8 matrix cores). Results of either meet the same accuracy contract. */
+ * W4A8_KERNEL_TILED, the tiled kernel for many tokens per expert (64-, 128- or 256-row
+ * tiles x 256 weight rows, bound by the 16-bit matrix cores). Both take the same exact
+ * products, so results of either meet the same accuracy contract. */
 #define W4A8_KERNEL_STREAM 0
 #define W4A8_KERNEL_TILED  1
 int32_t w4a8_moe_kernel(int32_t T);

@@ -81,7 +81,7 @@ def assert_final_close(out_gpu, out_ref):
 
 def assert_codes_consistent(c_gpu, c_ref, h_gpu, act, s_a, I, max_frac=1e-2, a_ref=None):
     """Requantized codes. The oracle's epilogue (activation, division by s_a, E4M3
-    rounding) applied to the GPU's own gate|up values must give the GPU's codes exactly;
+    rounding) applied to the GPU's own gate|up values must give the GPU's codes, every one;
     against the oracle's codes, differences may only come from the gate|up differences
     (checked separately to the 1e-4 bar), on at most max_frac of the codes: a differing
     code must be one that a value between the two activations rounds to (the rounding is
@@ -91,9 +91,9 @@ def assert_codes_consistent(c_gpu, c_ref, h_gpu, act, s_a, I, max_frac=1e-2, a_r
     a_own = activation(h[:, :I], act) * h[:, I:]
     own = quantize_static(a_own.astype(np.float32), s_a)
     own_eq = same_codes(own, c_gpu)
-    # fp32 activation vs fp64: only values within ~1e-7 of a rounding boundary may differ
-    assert 1.0 - own_eq.mean() <= 1e-4, "epilogue differs from the oracle's on the GPU's own gate|up"
-    _assert_adjacent(np.asarray(c_gpu)[~own_eq], own[~own_eq])
+    # the kernel takes every decision near a rounding boundary in double precision, with the
+    # oracle's formulas, from the same gate|up values: the codes are the same, all of them
+    assert own_eq.all(), f"{int((~own_eq).sum())} codes differ from the oracle's epilogue on the GPU's own gate|up"
     eq = same_codes(c_gpu, c_ref)
     frac = 1.0 - eq.mean()
     print(f"a codes: {frac:.4%} differ from the oracle's")
@@ -109,11 +109,7 @@ def assert_codes_consistent(c_gpu, c_ref, h_gpu, act, s_a, I, max_frac=1e-2, a_r
     a2 = np.asarray(a_ref, np.float64)[d].astype(np.float32)
     lo = e4m3_decode(quantize_static(np.minimum(a1, a2), s_a))
     hi = e4m3_decode(quantize_static(np.maximum(a1, a2), s_a))
-    # where the kernel's own rounding differs from the oracle's epilogue on the same gate|up
-    # (checked above: neighbours, at most 1e-4 of the codes), the oracle epilogue's code
-    # stands in for it
-    code = np.where(own_eq[d], np.asarray(c_gpu, np.uint8)[d], own[d])
-    got = e4m3_decode(code)
+    got = e4m3_decode(np.asarray(c_gpu, np.uint8)[d])
     ok = (got >= lo) & (got <= hi)
     assert ok.all(), f"{(~ok).sum()} codes not explained by the gate|up difference"
 

@@ -147,21 +147,21 @@ def _oracle_scales(cfg, x, logits, p13, p2):
 
 
 def _check_final(cfg, x, logits, s_x, p13, p2, s_a, ref, a, out):
-    """The requantized codes are decided on the kernel's own gate|up, so a code at a rounding
-    boundary may differ from the oracle's (checked by assert_codes_consistent). The final
-    output is held to the full bar against the oracle's down projection and combine of the
-    kernel's codes, and to the 1e-2 bar against the oracle's end-to-end result."""
+    """The layer's output against the oracle's end-to-end result (its own gate|up, its own
+    requantized codes, its own down projection and combine): the full bar, 1e-2 x max|ref|
+    everywhere and at most 0.1% of the elements above 1e-3 x max|ref|. As a separate check
+    of the down call alone, the output also meets the full bar against the oracle's down
+    projection and combine of the kernel's own codes."""
     same = oracle.moe_forward(x, logits, s_x, p13, p2, cfg.act, s_a, cfg.out_f32, a_codes_given=host(a))
     if cfg.out_f32:
         got, want, e2e = host(out), same["out"].astype(np.float32), ref["out"].astype(np.float32)
     else:
         got = bf16_bits_to_f64(host(out))
         want, e2e = bf16_bits_to_f64(same["out_rounded"]), bf16_bits_to_f64(ref["out_rounded"])
+    print("end to end:", end=" ")
+    assert_final_close(got, e2e)
+    print("down call on the kernel's codes:", end=" ")
     assert_final_close(got, want)
-    m = np.max(np.abs(e2e))
-    d = np.abs(np.asarray(got, np.float64) - e2e)
-    print(f"end to end: max err {d.max() / m:.3g} x max|ref|, {np.mean(d > 1e-3 * m):.4%} above 1e-3", flush=True)
-    assert d.max() <= 1e-2 * m
 
 
 LAYER_CASES = [
@@ -265,11 +265,13 @@ def test_moe_prefill_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-def test_integer_case_gate_up_bit_exact():
+@pytest.mark.parametrize("T", [20, 130, 600])
+def test_integer_case_gate_up_bit_exact(T):
     """Integer x and w, max |w| = 7 per row, s_x = 1: fp32 accumulation is exact in any
-    order, so gate|up must equal the integer product exactly."""
-    rng = np.random.default_rng(77)
-    T, H, I, E = 20, 384, 256, 4
+    order, so gate|up must equal the integer product exactly (20 tokens: the streaming
+    kernel; 130 and 600: the tiled kernel with 64- and 256-row tiles)."""
+    rng = np.random.default_rng(77 + T)
+    H, I, E = 384, 256, 4
     xi = rng.integers(-16, 17, size=(T, H))
     w13i = rng.integers(-7, 8, size=(E, 2 * I, H))
     w13i[:, :, 3] = 7

@@ -27,6 +27,30 @@ def test_activation_closed_forms():
     assert np.max(np.abs(activation(g, ACT_GELU_TANH) - activation(g, ACT_GELU_ERF))) < 1e-3
 
 
+def test_activations_against_torch():
+    """Each activation against torch's own implementation of the same function (an
+    independent library routine), in float64 to 1e-12: silu, gelu (erf form) and gelu with
+    approximate="tanh" (the cubic coefficient 0.044715 and sqrt(2/pi) of the tanh form)."""
+    import torch
+    g = np.concatenate([np.linspace(-12, 12, 4001), [-3.0, -2.0, -1.0, -0.5, 0.5, 1.0, 2.0, 3.0]])
+    t = torch.from_numpy(g)
+    F = torch.nn.functional
+    for act, ref in ((ACT_SILU, F.silu(t)), (ACT_GELU_ERF, F.gelu(t)), (ACT_GELU_TANH, F.gelu(t, approximate="tanh"))):
+        ref = ref.numpy()
+        got = activation(g, act)
+        assert np.all(np.abs(got - ref) <= 1e-12 * np.maximum(1.0, np.abs(ref))), act
+
+
+def test_gelu_tanh_identities():
+    """The tanh form through an independent algebraic path: 1/2 (1 + tanh y) = sigma(2 y), so
+    gelu_tanh(g) = g * expit(2 sqrt(2/pi) (g + 0.044715 g^3)); and it meets gelu_tanh(g) -
+    gelu_tanh(-g) = g."""
+    g = np.linspace(-9, 9, 3601)
+    y = math.sqrt(2.0 / math.pi) * (g + 0.044715 * g * g * g)
+    assert np.allclose(activation(g, ACT_GELU_TANH), g * expit(2.0 * y), rtol=1e-12, atol=1e-14)
+    assert np.allclose(activation(g, ACT_GELU_TANH) - activation(-g, ACT_GELU_TANH), g, rtol=1e-13, atol=1e-13)
+
+
 def test_lipschitz_constants():
     # silu' peaks at about 1.0998 near g = 2.4; gelu_erf' = Phi(g) + g phi(g) peaks at g = sqrt 2
     assert abs(act_lipschitz(ACT_SILU) - 1.0998) < 1e-3

@@ -77,6 +77,7 @@ void plan_decode(MoeGemmParams& p, bool gateup);
 void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 bool prefill_available();
+int prefill_token_blocks(int P, int E);   // 16-row token blocks per tile of the tiled kernel
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 // combine: out[t] = w0 * sum_s partial[s][pair_pos[2t]] + w1 * sum_s partial[s][pair_pos[2t+1]]

@@ -8,23 +8,8 @@
 // per-channel weight scale and the static activation scale are constant along K, so
 // they are applied once, in the epilogue.
 //
-// Which matrix core. gfx950's fp8 MFMA (16x16x128 f8f6f4, and the older 16x16x32 fp8)
-// sums each instruction's products with about 14 bits of precision below the largest
-// product of the instruction (measured on MI355X: 256 + 127 * 2^-9 comes out as
-// 256.234375), while its 16-bit MFMAs return exact fp32 sums for these operands. An
-// E4M3 value and an int4 code are both exact in fp16, so this kernel, which is bound
-// by HBM and leaves the matrix cores mostly idle, multiplies them on the fp16 MFMA
-// (16x16x32) and accumulates exactly as the method states. The tiled prefill kernel,
-// bound by the matrix cores, uses the fp8 MFMA.
-//
-// int4 -> fp16 in registers, 10 VALU ops per 8 weights, exact: flipping the top bit of a
-// nibble turns q into c = q + 8 in [0, 15]; a byte permute places the low nibbles' c under
-// the fp16 exponent of 1024 (bits 0x6400 | c = 1024 + c, two values per op) and one packed
-// fp16 subtraction of 1032 leaves q. The high nibbles stay where they are (1024 + 16 c,
-// minus 1152: 16 q), and the activations they meet are staged divided by 16, so no shift
-// is needed. (Codes placed as fp16 subnormals would need no subtraction, but the fp16
-// MFMA loses precision on subnormal operands: measured on MI355X, a K = 14336 down
-// projection erred by 5e-6 of its largest output instead of 1e-8.)
+// Which matrix core: the fp16 MFMA (16x16x32) on the exact values (common.h: the fp8
+// MFMA's sums are not exact; E4M3 values and int4 codes are exact in fp16).
 //
 // Mapping. A workgroup = 8 waves on one expert and one K-slice. The activation rows of
 // the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS as their
@@ -65,46 +50,6 @@ static_assert(kBody % kDepth == 0, "the loop body holds whole rounds");
 // chunk loop could not advance)
 static_assert(kDecodeLds / (16 * kDecodeMaxTiles) >= 128 * kDepth, "LDS chunk below one round");
 constexpr int kWeightLoadAux = W4A8_DECODE_NT_LOADS ? 2 : 0;   // cache-policy bits: nt
-typedef _Float16 v8h __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ uint4 ld16(const uint8_t* p) { return *reinterpret_cast<const uint4*>(p); }
-
-// two E4M3 codes (bytes 0,1 or, with HIGH, bytes 2,3) -> two fp16 values, exact
-template <bool HIGH>
-__device__ __forceinline__ uint32_t cvt2_e4m3_f16(uint32_t codes, float scale = 1.0f) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)codes, scale, HIGH));
-}
-
-typedef _Float16 v2h __attribute__((ext_vector_type(2)));
-
-// bytes 0,1 (SEL 0x04010400) or 2,3 (SEL 0x04030402) of x placed under the fp16 exponent
-// of 1024: the pair 1024 + x_byte (exact for any byte)
-template <uint32_t SEL>
-__device__ __forceinline__ v2h f16_1024_plus(uint32_t x) {
-  return __builtin_bit_cast(v2h, __builtin_amdgcn_perm(0x64646464u, x, SEL));
-}
-
-// One packed word (8 int4 codes, reorder layout) -> 8 exact fp16 values in K order:
-// q for elements 0..3 and 16 q for elements 4..7 (whose activations are staged / 16).
-// c = q + 8 is the nibble with its top bit flipped; the low nibbles give 1024 + c, the
-// high nibbles, left in place, 1024 + 16 c.
-__device__ __forceinline__ v8h int4x8_to_f16(uint32_t w, uint32_t mlo, uint32_t mhi) {
-  const uint32_t lo = (w ^ 0x88888888u) & mlo;                   // c of elements 0..3
-  const uint32_t hi = (w ^ 0x88888888u) & mhi;                   // 16 c of elements 4..7
-  const v2h off_lo = {(_Float16)1032.0f, (_Float16)1032.0f};     // 1024 + 8
-  const v2h off_hi = {(_Float16)1152.0f, (_Float16)1152.0f};     // 1024 + 16 * 8
-  const v2h e01 = f16_1024_plus<0x04010400u>(lo) - off_lo, e23 = f16_1024_plus<0x04030402u>(lo) - off_lo;
-  const v2h e45 = f16_1024_plus<0x04010400u>(hi) - off_hi, e67 = f16_1024_plus<0x04030402u>(hi) - off_hi;
-  v8h r;
-  r[0] = e01[0]; r[1] = e01[1]; r[2] = e23[0]; r[3] = e23[1];
-  r[4] = e45[0]; r[5] = e45[1]; r[6] = e67[0]; r[7] = e67[1];
-  return r;
-}
-
-__device__ __forceinline__ v4f mfma_f16(v8h a, v8h b, v4f c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ uint32_t word_of(const uint4& q, int m) {
   return m == 0 ? q.x : (m == 1 ? q.y : (m == 2 ? q.z : q.w));
 }
@@ -122,14 +67,6 @@ __device__ __forceinline__ uint4 buf_ld16_step(__amdgpu_buffer_rsrc_t r, uint32_
       uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), kWeightLoadAux));
 }
 
-
-// 8 E4M3 codes (one 8-byte half of a 16-byte LDS slot) -> the fp16 B operand of one
-// MFMA, exact; codes 4..7 face the weights' high nibbles (16 q) and are divided by 16
-// (E4M3 keeps 3 mantissa bits, so the quotient is an exact fp16 normal).
-__device__ __forceinline__ v8h e4m3x8_to_f16(uint32_t lo4, uint32_t hi4) {
-  return __builtin_bit_cast(v8h, make_uint4(cvt2_e4m3_f16<false>(lo4), cvt2_e4m3_f16<true>(lo4),
-                                            cvt2_e4m3_f16<false>(hi4, 0.0625f), cvt2_e4m3_f16<true>(hi4, 0.0625f)));
-}
 
 // One k-step (128 K) of one wave: 4 MFMAs of K = 32 per weight block and column tile
 // (the first nt of NT tiles). B comes from the E4M3 LDS chunk: per (tile, k-step) two
@@ -325,7 +262,7 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
       for (int v = 0; v < 4; ++v) {
         gv[v] = acc0[j][v] * k0 * sgv[v];
         uv[v] = acc1[j][v] * k0 * suv[v];
-        av[v] = div_rn(act_fast_rt(gv[v], p.act_fn) * uv[v], p.s_a, p.inv_s_a);
+        av[v] = requant_value_rt(gv[v], uv[v], p.s_a, p.inv_s_a, p.act_fn);
       }
       *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
       if (p.dbg) {

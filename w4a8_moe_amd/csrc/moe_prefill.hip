@@ -3,41 +3,32 @@
 //
 // The method ("INT4 MoE weights, FP8 compute", page "ROCm: enable trillion-parameter
 // MoE models with INT4-FP8 single node"; int4 weights upcast to float8 for fp8 math,
-// page "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm"): int4 codes are
-// turned into exact E4M3 codes and multiplied against the E4M3 activations on the fp8
-// MFMA (16x16x128), accumulating in fp32; the per-channel and static scales are applied
-// in the epilogue.
+// page "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm"): every product
+// is an E4M3 activation times an int4 weight code, summed in fp32; the per-channel and
+// static scales are applied in the epilogue. The products run on the fp16 MFMA
+// (16x16x32), whose sums of these exact values are exact (common.h: the fp8 MFMA's are
+// not, and its error breaks the output tolerance): int4 codes are widened to exact fp16
+// by exponent placement, E4M3 codes by the hardware conversion (those facing a weight's
+// high nibble divided by 16, exact).
 //
-// Conversion. Each int4 code becomes its exact E4M3 code by a table lookup on the byte
-// permute unit: for the 4 low (or high) nibbles of a word, one v_perm picks the codes of
-// 0..7, one the codes of -8..-1, and a third picks between them by the sign bit. The
-// products are then the exact q * x, so the accumulation error is that of the fp8
-// instruction on these products alone. (Offset codes q + 8, three bit operations per
-// word, would need the row sums of x taken back out, and the instruction's error grows
-// with the sum of |products|, about six times larger with the offset: that failed the
-// output tolerance.)
+// Tile. A workgroup computes TB blocks of 16 sorted rows (tokens of one expert; 64, 128
+// or 256 rows, chosen by the rows per expert) x 256 weight rows, K in steps of 128, with
+// 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against all TB token blocks, so
+// its int4 codes go from global memory straight into its own registers, are widened there
+// and used as MFMA operands without an LDS round trip. For gate|up the 64 rows are 32
+// gate channels and the 32 matching up channels, so act(gate) * up is formed in
+// registers. Only the token tile (TB*16 x 128 E4M3 codes per k-step, gathered through
+// sorted_pair for gate|up) is shared through LDS, double buffered, in MFMA operand order
+// with an XOR swizzle that keeps both the staging writes and the operand reads free of
+// bank conflicts; it stays E4M3 there (half the LDS traffic of fp16) and each wave widens
+// the operands it reads.
 //
-// Tile. A workgroup computes 256 sorted rows (tokens of one expert) x 256 weight rows,
-// K in steps of 128, with 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against
-// all 256 tokens (16 blocks), so its int4 codes go from global memory straight into its
-// own registers, are converted there and are used as MFMA operands without an LDS round
-// trip. For
-// gate|up the 64 rows are 32 gate channels and the 32 matching up channels, so
-// act(gate) * up is formed in registers. Only the token tile (256 x 128 E4M3 codes per
-// k-step, gathered through sorted_pair for gate|up) is shared through LDS, double
-// buffered, in MFMA operand order with an XOR swizzle that keeps both the staging writes
-// and the operand reads free of bank conflicts.
-//
-// Pipeline, per k-step s (one barrier each):
-//   * store the tokens of step s+1 (loaded one step earlier) into the other LDS buffer,
-//     issue the token loads of step s+2,
-//   * 64 MFMAs of step s, with the conversion of step s+1's weights (loaded two steps
-//     earlier) and the weight loads of step s+3 in between.
+// Pipeline, per k-step s (one barrier each): widen the step's 16 weight words (4 blocks x
+// 4 MFMAs of K = 32) and issue the weight loads of step s+2; then walk the token blocks,
+// the next block's operands read ahead, storing the tokens of step s+1 (loaded one step
+// earlier) into the other LDS buffer and issuing the token loads of step s+2 on the way.
 // Loads past the last k-step read in-bounds data or zeros and are never used, so the
 // loop has no branches.
-//
-// Accumulation note: gfx950's fp8 MFMA keeps about 14 bits below the largest product of
-// an instruction, so results differ from exact fp32 sums by about 1e-5 of the row scale.
 #include <algorithm>
 
 #include "common.h"
@@ -45,59 +36,18 @@
 
 namespace w4a8 {
 
-constexpr int kTB = 16;           // token blocks of 16 rows per tile
-constexpr int kPM = 16 * kTB;     // sorted rows per tile
 constexpr int kPN = 256;          // weight rows per tile
 constexpr int kPThreads = 256;    // 4 waves, 64 weight rows each
-constexpr int kTJ = kPM * 8 / kPThreads;                  // 16-byte token chunks per thread and k-step
-constexpr int kPTokBytes = kTB * 2048;                    // blocks of 16 rows x 128 codes
-constexpr int kPLds = 2 * kPTokBytes;                      // two token buffers
 constexpr int kGroupM = 4;        // M-tiles per band of the tile order
 constexpr uint32_t kPOutOfRange = 0x80000000u;   // past every buffer (all are < 2^31 bytes)
 
-__device__ __forceinline__ uint4 pf_ld16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
 // per-lane offset plus a wave-uniform one (the step), added by the load itself
 __device__ __forceinline__ uint4 pf_ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 0));
 }
 
-// Four two's-complement nibbles (sel = nibble & 7 per byte, sgn = 4 * sign bit per byte)
-// -> four exact E4M3 codes: 0..7 -> 00 38 40 44 48 4A 4C 4E, -8..-1 -> D0 CE CC CA C8 C4
-// C0 B8. The last permute takes byte i from the positive (selector i) or the negative
-// (selector 4 + i) table.
-__device__ __forceinline__ uint32_t e4m3_of_nibbles(uint32_t sel, uint32_t sgn) {
-  const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
-  const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
-  return __builtin_amdgcn_perm(neg, pos, sgn | 0x03020100u);
-}
-
-// One packed word (byte b: element b in the low nibble, element 4+b in the high nibble)
-// -> E4M3 codes of elements 0..3 (lo) and 4..7 (hi).
-__device__ __forceinline__ uint32_t e4m3_of_nibbles_sel(uint32_t sel, uint32_t selsgn) {
-  const uint32_t pos = __builtin_amdgcn_perm(0x4E4C4A48u, 0x44403800u, sel);
-  const uint32_t neg = __builtin_amdgcn_perm(0xB8C0C4C8u, 0xCACCCED0u, sel);
-  return __builtin_amdgcn_perm(neg, pos, selsgn);
-}
-__device__ __forceinline__ void int4x8_to_e4m3(uint32_t w, uint32_t& lo, uint32_t& hi, uint32_t m4 = 0x04040404u,
-                                               uint32_t id = 0x03020100u) {
-  const uint32_t w4 = w >> 4;
-  lo = e4m3_of_nibbles_sel(w & 0x07070707u, ((w >> 1) & m4) | id);
-  hi = e4m3_of_nibbles_sel(w4 & 0x07070707u, ((w4 >> 1) & m4) | id);
-}
-
-__device__ __forceinline__ v8i int4x32_to_e4m3(uint4 q) {
-  const uint32_t w[4] = {q.x, q.y, q.z, q.w};
-  v8i a;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    uint32_t lo, hi;
-    int4x8_to_e4m3(w[t], lo, hi);
-    a[2 * t] = (int)lo;
-    a[2 * t + 1] = (int)hi;
-  }
-  return a;
+__device__ __forceinline__ uint32_t word4(const uint4& q, int m) {
+  return m == 0 ? q.x : (m == 1 ? q.y : (m == 2 ? q.z : q.w));
 }
 
 struct TileOrigin {
@@ -105,13 +55,14 @@ struct TileOrigin {
 };
 
 // Linear M-tile index -> (expert, first row). Returns false past the last tile.
-__device__ __forceinline__ bool locate_mtile(const int32_t* __restrict__ offsets, int E, int mt, TileOrigin& o) {
+__device__ __forceinline__ bool locate_mtile(const int32_t* __restrict__ offsets, int E, int pm, int mt,
+                                             TileOrigin& o) {
   int before = 0;
   for (int e = 0; e < E; ++e) {
     const int s0 = offsets[e], c = offsets[e + 1] - s0;
-    const int nt = (c + kPM - 1) / kPM;
+    const int nt = (c + pm - 1) / pm;
     if (mt < before + nt) {
-      o.e = e; o.seg0 = s0; o.cnt = c; o.m0 = (mt - before) * kPM;
+      o.e = e; o.seg0 = s0; o.cnt = c; o.m0 = (mt - before) * pm;
       return true;
     }
     before += nt;
@@ -125,10 +76,14 @@ __device__ __forceinline__ bool locate_mtile(const int32_t* __restrict__ offsets
 // consecutive staging lanes (two rows x four K-parts x two halves).
 __device__ __forceinline__ int tok_slot(int i, int g, int h) { return 16 * g + (i ^ (2 * g + 8 * h)); }
 
-// ACT: the gated activation (gate|up only), a template parameter so that each instance
-// carries the code of one activation in its unrolled epilogue.
-template <bool GATEUP, int ACT>
+// TB: token blocks of 16 rows per tile. ACT: the gated activation (gate|up only), a template
+// parameter so that each instance carries the code of one activation in its epilogue.
+template <bool GATEUP, int ACT, int TB>
 __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles) {
+  constexpr int kPM = 16 * TB;                       // sorted rows per tile
+  constexpr int kTJ = kPM * 8 / kPThreads;           // 16-byte token chunks per thread and k-step
+  constexpr int kTokBytes = TB * 2048;               // blocks of 16 rows x 128 codes
+  static_assert(kTJ * 2 == TB, "one token chunk per two token blocks");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
@@ -145,7 +100,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   const int gm = min(kGroupM, mtiles_upper - band * kGroupM);
   const int mt = band * kGroupM + rem % gm, ntile = rem / gm;
   TileOrigin o;
-  if (!locate_mtile(p.offsets, p.E, mt, o)) return;
+  if (!locate_mtile(p.offsets, p.E, kPM, mt, o)) return;
   const int rows = min(kPM, o.cnt - o.m0);                  // valid sorted rows in this tile
   // first channel of the tile: gate|up -> 128 channels (gate rows + the matching up rows)
   const int n0 = GATEUP ? ntile * (kPN / 2) : ntile * kPN;
@@ -185,11 +140,11 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     const int pg = part >> 1, ph = part & 1;
     tdst[j] = (r >> 4) * 2048 + ph * 1024 + tok_slot(r & 15, pg, ph) * 16;
   }
-  const int rd0 = tok_slot(i, g, 0) * 16, rd1 = 1024 + tok_slot(i, g, 1) * 16;
+  const int rd[2] = {tok_slot(i, g, 0) * 16, 1024 + tok_slot(i, g, 1) * 16};
 
-  v4f acc[kTB][4];
+  v4f acc[TB][4];
 #pragma unroll
-  for (int bb = 0; bb < kTB; ++bb)
+  for (int bb = 0; bb < TB; ++bb)
 #pragma unroll
     for (int a = 0; a < 4; ++a) acc[bb][a] = v4f{0.f, 0.f, 0.f, 0.f};
 
@@ -200,73 +155,62 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 #pragma unroll
     for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16s(tr, toff[j], (uint32_t)(s * 128));
   };
-  auto store_tokens = [&](int buf) {
+  uint4 wc[4], wn[4];          // raw weights of steps s and s+1
 #pragma unroll
-    for (int j = 0; j < kTJ; ++j) *reinterpret_cast<uint4*>(lds + buf * kPTokBytes + tdst[j]) = tq[j];
-  };
-  uint4 w0[4], w1[4];          // raw weights of steps s and s+1
-  auto load_weights = [&](uint4 (&w)[4], int s) {
-#pragma unroll
-    for (int a = 0; a < 4; ++a) w[a] = pf_ld16s(wr, woff[a], (uint32_t)(s * kTileBytes));
-  };
-
-  // ---- prologue: weights of steps 0..2 in flight, tokens of step 0 in LDS, of step 1 in flight
-  load_weights(w0, 0);
-  load_weights(w1, 1);
+  for (int a = 0; a < 4; ++a) {
+    wc[a] = pf_ld16s(wr, woff[a], 0);
+    wn[a] = pf_ld16s(wr, woff[a], kTileBytes);
+  }
   load_tokens(0);
-  store_tokens(0);
-  load_tokens(1);
-  v8i aop[4];
 #pragma unroll
-  for (int a = 0; a < 4; ++a) aop[a] = int4x32_to_e4m3(w0[a]);
+  for (int j = 0; j < kTJ; ++j) *reinterpret_cast<uint4*>(lds + tdst[j]) = tq[j];
+  load_tokens(1);
   lds_barrier();
 
-  // One k-step per iteration (a single loop body keeps every accumulator in place). The
-  // token blocks are walked with the next block's operand read ahead; into each block's 4
-  // MFMAs go one token store (step s+1) or one token load (step s+2) and one or two of the
-  // 16 words of the step s+1 weight conversion; a weight block's raw registers are
-  // reloaded with step s+2 as soon as its last word is converted. Scheduling barriers keep
-  // the compiler from hoisting every LDS read to the top.
-  // the two byte masks of the conversion live in registers, so that mask-and-merge is one
-  // 3-input bit operation
-  uint32_t km4 = 0x04040404u, kid = 0x03020100u;
-  asm volatile("" : "+v"(km4), "+v"(kid));
+  // the two nibble masks of the widening live in registers (one 3-input bit op per mask)
+  uint32_t mlo = 0x0F0F0F0Fu, mhi = 0xF0F0F0F0u;
+  asm volatile("" : "+v"(mlo), "+v"(mhi));
   for (int s = 0; s < steps; ++s) {
-    const int cur = s & 1;
-    const uint8_t* T = lds + cur * kPTokBytes;
-    uint8_t* Tn = lds + (cur ^ 1) * kPTokBytes;
-    v8i anext[4];
-    v8i bcur = operand_from(*reinterpret_cast<const uint4*>(T + rd0), *reinterpret_cast<const uint4*>(T + rd1));
+    const uint8_t* Tc = lds + (s & 1) * kTokBytes;
+    uint8_t* Tn = lds + ((s & 1) ^ 1) * kTokBytes;
+    // this step's weight operands: word m of block a -> K 32 g + 8 m .. +8 of its rows
+    v8h A[4][4];
 #pragma unroll
-    for (int bb = 0; bb < kTB; ++bb) {
-      v8i bnext;
-      if (bb < kTB - 1)
-        bnext = operand_from(*reinterpret_cast<const uint4*>(T + (bb + 1) * 2048 + rd0),
-                             *reinterpret_cast<const uint4*>(T + (bb + 1) * 2048 + rd1));
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_fp8_16x16x128(aop[a], bcur, acc[bb][a]);
-      const int j = bb >> 1;
-      if ((bb & 1) == 0)
-        *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                     // step s+1
-      else
-        tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((s + 2) * 128));             // step s+2
+      for (int a = 0; a < 4; ++a) A[m][a] = int4x8_to_f16(word4(wc[a], m), mlo, mhi);
 #pragma unroll
-      for (int wi = bb; wi < 16; wi += kTB) {
-        const int a = wi >> 2, tw = wi & 3;
-        const uint32_t w = tw == 0 ? w1[a].x : tw == 1 ? w1[a].y : tw == 2 ? w1[a].z : w1[a].w;
-        uint32_t lo, hi;
-        int4x8_to_e4m3(w, lo, hi, km4, kid);
-        anext[a][2 * tw] = (int)lo;
-        anext[a][2 * tw + 1] = (int)hi;
-      }
-      // words wi are converted at bb = wi (16 blocks): block a's last word goes at bb = 4 a + 3
-      static_assert(kTB == 16, "the reload points below follow the conversion order for 16 blocks");
-      if ((bb & 3) == 3) w1[bb >> 2] = pf_ld16s(wr, woff[bb >> 2], (uint32_t)((s + 2) * kTileBytes));
-      __builtin_amdgcn_sched_barrier(0);
-      if (bb < kTB - 1) bcur = bnext;
+    for (int a = 0; a < 4; ++a) {
+      wc[a] = wn[a];
+      wn[a] = pf_ld16s(wr, woff[a], (uint32_t)((s + 2) * kTileBytes));
     }
+    // token blocks in order, each block's 16 MFMAs (4 K-parts x 4 weight blocks) together:
+    // an accumulator's four MFMAs of the step are adjacent, which keeps every accumulator in
+    // place (spread over the step, the register allocator rotates them through copies)
+    uint4 b0 = *reinterpret_cast<const uint4*>(Tc + rd[0]);
+    uint4 b1 = *reinterpret_cast<const uint4*>(Tc + rd[1]);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) aop[a] = anext[a];
+    for (int bb = 0; bb < TB; ++bb) {
+      uint4 n0, n1;
+      if (bb + 1 < TB) {
+        n0 = *reinterpret_cast<const uint4*>(Tc + (bb + 1) * 2048 + rd[0]);
+        n1 = *reinterpret_cast<const uint4*>(Tc + (bb + 1) * 2048 + rd[1]);
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint4& bq = m < 2 ? b0 : b1;
+        const v8h B = (m & 1) ? e4m3x8_to_f16(bq.z, bq.w) : e4m3x8_to_f16(bq.x, bq.y);
+#pragma unroll
+        for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_f16(A[m][a], B, acc[bb][a]);
+      }
+      if ((bb & 1) == 0) {
+        const int j = bb >> 1;
+        *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                   // step s+1
+        tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((s + 2) * 128));           // step s+2
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (bb + 1 < TB) { b0 = n0; b1 = n1; }
+    }
     lds_barrier();
   }
 
@@ -289,7 +233,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   // Values are computed for every (row, channel) of the lane, uniformly; only the stores
   // are guarded (rows and channels past the tile's valid range hold zero sums).
 #pragma unroll
-  for (int bb = 0; bb < kTB; ++bb) {
+  for (int bb = 0; bb < TB; ++bb) {
     const int rt = 16 * bb + i;                              // row within the tile
     const bool row_ok = rt < rows;
     const size_t r = (size_t)(o.seg0 + o.m0 + (row_ok ? rt : 0));   // sorted row
@@ -305,7 +249,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
         for (int v = 0; v < 4; ++v) {
           gv[v] = acc[bb][a][v] * sgv[v];
           uv[v] = acc[bb][a + 2][v] * suv[v];
-          av[v] = div_rn(act_fast<ACT>(gv[v]) * uv[v], p.s_a, p.inv_s_a);
+          av[v] = requant_value<ACT>(gv[v], uv[v], p.s_a, p.inv_s_a);
         }
         const uint32_t codes = pack4_e4m3(av[0], av[1], av[2], av[3]);
         if (row_ok && nb < p.n_out) {
@@ -332,19 +276,41 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 
 bool prefill_available() { return true; }
 
-void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
+// Token blocks per tile: the smallest of 4, 8, 16 that holds the mean rows per expert with
+// rows (P / E), so that an expert's weights are read by as few M-tiles as possible without
+// running the matrix cores on padding rows.
+int prefill_token_blocks(int P, int E) {
+  const int mean = (P + E - 1) / E;
+  return mean <= 64 ? 4 : (mean <= 128 ? 8 : 16);
+}
+
+template <int TB>
+static void launch_tb(const MoeGemmParams& p, bool gateup, hipStream_t st) {
+  constexpr int kPM = 16 * TB;
   // every expert's rows split into tiles of kPM; the count of tiles is at most P/kPM + E
   const int mtiles_upper = (p.P + kPM - 1) / kPM + p.E;
   const int ntiles = gateup ? (p.n_out + kPN / 2 - 1) / (kPN / 2) : (p.Nw + kPN - 1) / kPN;
   const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles);
+  const size_t lds = 2 * TB * 2048;
   if (!gateup)
-    hipLaunchKernelGGL((moe_prefill_kernel<false, 0>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+    hipLaunchKernelGGL((moe_prefill_kernel<false, 0, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+                       ntiles);
   else if (p.act_fn == 0)
-    hipLaunchKernelGGL((moe_prefill_kernel<true, 0>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 0, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+                       ntiles);
   else if (p.act_fn == 1)
-    hipLaunchKernelGGL((moe_prefill_kernel<true, 1>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 1, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+                       ntiles);
   else
-    hipLaunchKernelGGL((moe_prefill_kernel<true, 2>), dim3(grid), dim3(kPThreads), kPLds, st, p, mtiles_upper, ntiles);
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 2, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+                       ntiles);
+}
+
+void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
+  const int tb = prefill_token_blocks(p.P, p.E);
+  if (tb == 4) launch_tb<4>(p, gateup, st);
+  else if (tb == 8) launch_tb<8>(p, gateup, st);
+  else launch_tb<16>(p, gateup, st);
 }
 
 }  // namespace w4a8
