@@ -17,11 +17,10 @@
 // its int4 codes go from global memory straight into its own registers, are widened there
 // and used as MFMA operands without an LDS round trip. For gate|up the 64 rows are 32
 // gate channels and the 32 matching up channels, so act(gate) * up is formed in
-// registers. Only the token tile (TB*16 x 128 E4M3 codes per k-step, gathered through
-// sorted_pair for gate|up) is shared through LDS, double buffered, in MFMA operand order
-// with an XOR swizzle that keeps both the staging writes and the operand reads free of
-// bank conflicts; it stays E4M3 there (half the LDS traffic of fp16) and each wave widens
-// the operands it reads.
+// registers. Only the token tile (TB*16 rows x 128 K per k-step, gathered through
+// sorted_pair for gate|up) is shared through LDS, double buffered: each thread widens its
+// staging chunks to fp16 once, and the waves read finished MFMA operands (1 KB per token
+// block and K-part, lane l's 16 bytes at 16 l: no bank conflicts on either side).
 //
 // Pipeline, per k-step s (one barrier each): widen the step's 16 weight words (4 blocks x
 // 4 MFMAs of K = 32) and issue the weight loads of step s+2; then walk the token blocks,
@@ -29,6 +28,10 @@
 // earlier) into the other LDS buffer and issuing the token loads of step s+2 on the way.
 // Loads past the last k-step read in-bounds data or zeros and are never used, so the
 // loop has no branches.
+//
+// Measured on MI355X (Grok-1-shaped prefill, 256-row tiles): the matrix cores are busy
+// about 56% of the cycles; the step's other work (operand widening, staging, epilogue)
+// adds to the MFMA time rather than hiding under it with one wave per SIMD.
 #include <algorithm>
 
 #include "common.h"
@@ -82,7 +85,7 @@ template <bool GATEUP, int ACT, int TB>
 __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles) {
   constexpr int kPM = 16 * TB;                       // sorted rows per tile
   constexpr int kTJ = kPM * 8 / kPThreads;           // 16-byte token chunks per thread and k-step
-  constexpr int kTokBytes = TB * 2048;               // blocks of 16 rows x 128 codes
+  constexpr int kTokBytes = TB * 4096;               // blocks of 16 rows x 128 K, fp16
   static_assert(kTJ * 2 == TB, "one token chunk per two token blocks");
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id();
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     woff[a] = chan < (GATEUP ? p.n_out : p.Nw) ? (uint32_t)(grow - i) * row_bytes + 16 * lane : kPOutOfRange;
   }
 
-  // ---- token staging: chunk c = tid + 256 j is tile row c / 8, 16-byte part c % 8.
+  // ---- token staging: each thread moves kTJ chunks of 16 E4M3 codes per k-step.
   // gate|up gathers token rows of x (T*H < 2^31 bytes); down reads the tile's own rows of
   // the sorted activation (the buffer starts at the tile, kPM*K < 2^31 bytes).
   const uint8_t* tbase = GATEUP ? p.act : p.act + (size_t)(o.seg0 + o.m0) * p.K;
@@ -130,18 +133,19 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   int tdst[kTJ];
 #pragma unroll
   for (int j = 0; j < kTJ; ++j) {
-    const int c = tid + kPThreads * j, r = c >> 3, part = c & 7;
+    // chunk c = tid + 256 j: row 16 (c >> 7) + c % 16, 16-byte part p = (c >> 4) & 7 (K 16 p..+16);
+    // 16 consecutive lanes take 16 rows of one part, so their LDS stores are consecutive
+    const int c = tid + kPThreads * j, r = 16 * (c >> 7) + (c & 15), part = (c >> 4) & 7;
     uint32_t off = kPOutOfRange;
     if (r < rows) {
       const int srow = GATEUP ? (p.sorted_pair[o.seg0 + o.m0 + r] >> 1) : r;
       off = (uint32_t)srow * p.K + part * 16;
     }
     toff[j] = off;
-    const int pg = part >> 1, ph = part & 1;
-    tdst[j] = (r >> 4) * 2048 + ph * 1024 + tok_slot(r & 15, pg, ph) * 16;
+    // part p holds K-parts m = 2 (p & 1), +1 of lane group g = p >> 1 (K 32 g + 8 m .. +8)
+    tdst[j] = ((r >> 4) * 4 + 2 * (part & 1)) * 1024 + ((r & 15) + 16 * (part >> 1)) * 16;
   }
-  const int rd[2] = {tok_slot(i, g, 0) * 16, 1024 + tok_slot(i, g, 1) * 16};
-
+  const int rdl = lane * 16;
   v4f acc[TB][4];
 #pragma unroll
   for (int bb = 0; bb < TB; ++bb)
@@ -162,8 +166,12 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     wn[a] = pf_ld16s(wr, woff[a], kTileBytes);
   }
   load_tokens(0);
+  auto store_tokens = [&](uint8_t* T, int j) {
+    *reinterpret_cast<v8h*>(T + tdst[j]) = e4m3x8_to_f16(tq[j].x, tq[j].y);
+    *reinterpret_cast<v8h*>(T + tdst[j] + 1024) = e4m3x8_to_f16(tq[j].z, tq[j].w);
+  };
 #pragma unroll
-  for (int j = 0; j < kTJ; ++j) *reinterpret_cast<uint4*>(lds + tdst[j]) = tq[j];
+  for (int j = 0; j < kTJ; ++j) store_tokens(lds, j);
   load_tokens(1);
   lds_barrier();
 
@@ -187,29 +195,31 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
     // token blocks in order, each block's 16 MFMAs (4 K-parts x 4 weight blocks) together:
     // an accumulator's four MFMAs of the step are adjacent, which keeps every accumulator in
     // place (spread over the step, the register allocator rotates them through copies)
-    uint4 b0 = *reinterpret_cast<const uint4*>(Tc + rd[0]);
-    uint4 b1 = *reinterpret_cast<const uint4*>(Tc + rd[1]);
+    v8h Bc[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) Bc[m] = *reinterpret_cast<const v8h*>(Tc + m * 1024 + rdl);
 #pragma unroll
     for (int bb = 0; bb < TB; ++bb) {
-      uint4 n0, n1;
+      v8h Bn[4];
       if (bb + 1 < TB) {
-        n0 = *reinterpret_cast<const uint4*>(Tc + (bb + 1) * 2048 + rd[0]);
-        n1 = *reinterpret_cast<const uint4*>(Tc + (bb + 1) * 2048 + rd[1]);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Bn[m] = *reinterpret_cast<const v8h*>(Tc + ((bb + 1) * 4 + m) * 1024 + rdl);
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint4& bq = m < 2 ? b0 : b1;
-        const v8h B = (m & 1) ? e4m3x8_to_f16(bq.z, bq.w) : e4m3x8_to_f16(bq.x, bq.y);
 #pragma unroll
-        for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_f16(A[m][a], B, acc[bb][a]);
+        for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_f16(A[m][a], Bc[m], acc[bb][a]);
       }
       if ((bb & 1) == 0) {
         const int j = bb >> 1;
-        *reinterpret_cast<uint4*>(Tn + tdst[j]) = tq[j];                   // step s+1
+        store_tokens(Tn, j);                                               // step s+1
         tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((s + 2) * 128));           // step s+2
       }
       __builtin_amdgcn_sched_barrier(0);
-      if (bb + 1 < TB) { b0 = n0; b1 = n1; }
+      if (bb + 1 < TB) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) Bc[m] = Bn[m];
+      }
     }
     lds_barrier();
   }
@@ -280,6 +290,10 @@ bool prefill_available() { return true; }
 // rows (P / E), so that an expert's weights are read by as few M-tiles as possible without
 // running the matrix cores on padding rows.
 int prefill_token_blocks(int P, int E) {
+#ifdef W4A8_PREFILL_TB
+  (void)P; (void)E;
+  return W4A8_PREFILL_TB;
+#endif
   const int mean = (P + E - 1) / E;
   return mean <= 64 ? 4 : (mean <= 128 ? 8 : 16);
 }
@@ -291,7 +305,7 @@ static void launch_tb(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   const int mtiles_upper = (p.P + kPM - 1) / kPM + p.E;
   const int ntiles = gateup ? (p.n_out + kPN / 2 - 1) / (kPN / 2) : (p.Nw + kPN - 1) / kPN;
   const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles);
-  const size_t lds = 2 * TB * 2048;
+  const size_t lds = 2 * TB * 4096;
   if (!gateup)
     hipLaunchKernelGGL((moe_prefill_kernel<false, 0, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
                        ntiles);
