@@ -229,6 +229,26 @@ int32_t moe_gemm2_w4a8(const uint8_t* a_fp8, float s_a,
                        void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_gemm2_w4a8_noalloc -- moe_gemm2_w4a8 for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments and results without ws / ws_bytes. The split-K partials live in a
+ * library-owned device array of moe_gemm2_w4a8_noalloc_max_workspace() bytes (32 MiB), one
+ * per GPU, held until the process ends; the call allocates and frees nothing. Every call on
+ * one GPU shares that GPU's array, so calls that overlap on one GPU (other streams, other
+ * threads) race: serialize them. Its contents are left from the last call; this call
+ * writes every value it reads.
+ * Returns W4A8_ERR_WORKSPACE when w4a8_workspace_bytes(W4A8_OP_GEMM2, T, H, I, E) exceeds
+ * the array (decode batches fit: Grok-1-shaped T = 32 needs 12.6 MB; prefill-sized T does
+ * not), W4A8_ERR_HIP if the array's address cannot be obtained, else as moe_gemm2_w4a8.
+ */
+int32_t moe_gemm2_w4a8_noalloc(const uint8_t* a_fp8, float s_a,
+                               const int32_t* w2, const float* s_w2,
+                               const int32_t* offsets, const int32_t* pair_pos, const float* topk_w,
+                               int32_t T, int32_t H, int32_t I, int32_t E,
+                               int32_t out_dtype, void* out, void* stream);
+size_t moe_gemm2_w4a8_noalloc_max_workspace(void);
+
+/*
  * fp8_block_quant -- block-FP8 quantization of a dense bf16 weight (the FP8_PB_WO
  * layout of the page "qwen4_exp: serve the block-FP8 dense projections natively
  * (+25% decode)": e4m3 weight plus one fp32 scale per 128x128 block).

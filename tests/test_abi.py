@@ -18,6 +18,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = W.header_functions()
     assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_route_sort_quant", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
+                          "moe_gemm2_w4a8_noalloc", "moe_gemm2_w4a8_noalloc_max_workspace",
                           "fp8_block_quant", "fp8_block_linear", "fp8_tensor_quant", "fp8_linear_w8a8",
                           "fp8_kv_cache_store",
                           "w4a8_workspace_bytes", "w4a8_status_str", "w4a8_moe_kernel"}
@@ -146,6 +147,24 @@ def test_gemm2_validation(L):
     assert _g2(L, ws_bytes=need - 1) == W.ERR_WORKSPACE
     assert _g2(L, ws=None, ws_bytes=need) == W.ERR_NULL
     assert _g2(L, T=0) == W.OK
+
+
+def test_gemm2_noalloc_validation(L):
+    """The allocation-free down call rejects what the workspace call rejects, and a batch
+    whose split-K partials exceed the library's array, all before any HIP call."""
+    assert W.noalloc_max_workspace() == 32 << 20
+
+    def g(T=32, H=256, I=512, E=8, dt=W.DT_BF16, s_a=0.5, out=A, topk_w=A):
+        return L.moe_gemm2_w4a8_noalloc(A, s_a, A, A, A, A, topk_w, T, H, I, E, dt, out, None)
+    assert g(I=384 + 64) == W.ERR_SHAPE
+    assert g(dt=W.DT_E4M3) == W.ERR_ARG
+    assert g(s_a=0.0) == W.ERR_ARG
+    assert g(topk_w=None) == W.ERR_NULL
+    assert g(out=U) == W.ERR_ALIGN
+    assert g(T=0) == W.OK
+    # 2 T H 4 bytes of partials at least: 4096 tokens x 6144 channels is 192 MiB
+    assert W.workspace_bytes(W.OP_GEMM2, 4096, 6144, 32768, 8) > 32 << 20
+    assert g(T=4096, H=6144, I=32768) == W.ERR_WORKSPACE
 
 
 def test_block_validation(L):

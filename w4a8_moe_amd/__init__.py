@@ -41,6 +41,8 @@ _SIGNATURES = {
     "moe_gemm1_w4a8": (_I32, [_P, _I32, _F32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _P, _P,
                               _P, _SZ, _P]),
     "moe_gemm2_w4a8": (_I32, [_P, _F32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
+    "moe_gemm2_w4a8_noalloc": (_I32, [_P, _F32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
+    "moe_gemm2_w4a8_noalloc_max_workspace": (_SZ, []),
     "fp8_block_quant": (_I32, [_P, _I32, _I32, _P, _P, _P]),
     "fp8_block_linear": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "fp8_tensor_quant": (_I32, [_P, _I64, _P, _P, _P, _SZ, _P]),
@@ -282,6 +284,35 @@ def moe_gemm2_w4a8(a, s_a, w2, s_w2, offsets, pair_pos, topk_w, out_dtype="bf16"
                                                   _ptr(pair_pos), _ptr(topk_w), T, H, I, E, dt, _ptr(out),
                                                   _ptr(ws), ws.numel(), _stream(dev)))
     return out
+
+
+def moe_gemm2_w4a8_noalloc(a, s_a, w2, s_w2, offsets, pair_pos, topk_w, out_dtype="bf16", out=None):
+    """moe_gemm2_w4a8 with the library's own scratch in place of a workspace (the call
+    allocates nothing on the device; ``out`` is allocated here only when not given)."""
+    torch = _torch()
+    P, I = a.shape
+    T = P // 2
+    if w2.dim() != 4:
+        raise ValueError("w2: expected the tiled layout [E, H/16, I/128, 256] (w4_tile)")
+    E, HB, _, _ = w2.shape
+    H = HB * 16
+    _need(a, torch.uint8, (2 * T, I), "a_fp8")
+    _need(w2, torch.int32, (E, H // 16, I // 128, 256), "w2 (tiled)")
+    _need(s_w2, torch.float32, (E, H), "s_w2")
+    _need(offsets, torch.int32, (E + 1,), "offsets")
+    _need(pair_pos, torch.int32, (2 * T,), "pair_pos")
+    _need(topk_w, torch.float32, (T, 2), "topk_w")
+    dt = DT_BF16 if out_dtype in ("bf16", torch.bfloat16) else DT_F32
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if dt == DT_BF16 else torch.float32, device=a.device)
+    _check("moe_gemm2_w4a8_noalloc", lib().moe_gemm2_w4a8_noalloc(
+        _ptr(a), float(s_a), _ptr(w2), _ptr(s_w2), _ptr(offsets), _ptr(pair_pos), _ptr(topk_w), T, H, I, E, dt,
+        _ptr(out), _stream(a.device)))
+    return out
+
+
+def noalloc_max_workspace():
+    return int(lib().moe_gemm2_w4a8_noalloc_max_workspace())
 
 
 def fp8_block_quant(w):

@@ -4,6 +4,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/libw4a8moe.h"
 #include "kernels.h"
@@ -50,6 +51,30 @@ int gemm2_ksplit(int32_t T, int32_t H, int32_t I, int32_t E) {
 // gemm2 workspace: the split-K partials of the down projection
 size_t gemm2_ws(int32_t T, int32_t H, int32_t I, int32_t E) {
   return round_up((size_t)gemm2_ksplit(T, H, I, E) * 2 * T * H * sizeof(float), 256);
+}
+
+// ---- the allocation-free variant's scratch: the down projection's split-K partials in a
+// file-scope device array, one copy per GPU for the life of the process. Its address on
+// each device comes from hipGetSymbolAddress, taken once per device with that device
+// current; host code uses only that address (the array's own name is a host-side stand-in).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// The scratch array's device address on the current device, or nullptr on a HIP error.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
 }
 
 }  // namespace
@@ -249,6 +274,27 @@ int32_t moe_gemm2_w4a8(const uint8_t* a_fp8, float s_a, const int32_t* w2, const
   launch_combine(p.partial, ksplit, 2 * T, H, pair_pos, topk_w, T, out_dtype == W4A8_DT_BF16, out, s);
   return launch_status();
 }
+
+int32_t moe_gemm2_w4a8_noalloc(const uint8_t* a_fp8, float s_a, const int32_t* w2, const float* s_w2,
+                               const int32_t* offsets, const int32_t* pair_pos, const float* topk_w, int32_t T,
+                               int32_t H, int32_t I, int32_t E, int32_t out_dtype, void* out, void* stream) {
+  int32_t st = check_moe_shape(T, H, I, E);
+  if (st != W4A8_OK) return st;
+  if (out_dtype != W4A8_DT_BF16 && out_dtype != W4A8_DT_F32) return W4A8_ERR_ARG;
+  if (!good_scale(s_a)) return W4A8_ERR_ARG;
+  if (T == 0) return W4A8_OK;
+  if (!a_fp8 || !w2 || !s_w2 || !offsets || !pair_pos || !topk_w || !out) return W4A8_ERR_NULL;
+  if (!aligned16(a_fp8) || !aligned16(w2) || !aligned16(s_w2) || !aligned16(offsets) || !aligned16(pair_pos) ||
+      !aligned16(topk_w) || !aligned16(out))
+    return W4A8_ERR_ALIGN;
+  if (gemm2_ws(T, H, I, E) > kScratchBytes) return W4A8_ERR_WORKSPACE;
+  void* ws = scratch_address();                            // the first HIP call
+  if (ws == nullptr) return W4A8_ERR_HIP;
+  return moe_gemm2_w4a8(a_fp8, s_a, w2, s_w2, offsets, pair_pos, topk_w, T, H, I, E, out_dtype, out, ws,
+                        kScratchBytes, stream);
+}
+
+size_t moe_gemm2_w4a8_noalloc_max_workspace(void) { return kScratchBytes; }
 
 int32_t fp8_block_quant(const uint16_t* w_bf16, int32_t N, int32_t K, uint8_t* w_e4m3, float* scales,
                         void* stream) {
