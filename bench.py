@@ -43,6 +43,10 @@ def parse():
                     help="skip timing the block-FP8 GEMVs and the per-tensor FP8 linears")
     ap.add_argument("--no-prefill", action="store_true",
                     help="with the default decode workload, skip the prefill layer's line")
+    ap.add_argument("--no-grok-decode", action="store_true",
+                    help="with the default decode workload, skip the Grok-1-shaped decode layer's line")
+    ap.add_argument("--no-token-sweep", action="store_true",
+                    help="with the default decode workload, skip the 64..1024-token sweep of the two GEMMs")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -101,10 +105,11 @@ def gemm1_flops(cfg):
     return 2.0 * (2 * cfg.T) * (2 * cfg.I) * cfg.H
 
 
-def cpu_baseline(cfg, s_x, s_a, ids, max_tokens=32):
-    """The oracle on a bounded sample of the same workload: up to max_tokens of the tokens
-    routed to the most common expert pair of the batch (their two experts' weights packed
-    by the oracle, untimed); the timed part is the oracle's layer forward of those tokens."""
+def cpu_baseline(cfg, s_x, s_a):
+    """The oracle on the whole decode layer of the workload (every token, every expert):
+    each expert's weights are packed by the oracle (timed apart, beside the GPU's w4_pack),
+    and the timed part is the oracle's layer forward, which unpacks each expert's int4 rows
+    in chunks and sums exactly in fp64."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -113,31 +118,26 @@ def cpu_baseline(cfg, s_x, s_a, ids, max_tokens=32):
         blas_threads = 1
     x = synth.activations(cfg)
     logits = synth.router_logits(cfg)
-    pairs = [tuple(sorted(map(int, r))) for r in ids]
-    best = max(set(pairs), key=pairs.count)
-    toks = np.array([t for t, p in enumerate(pairs) if p == best], dtype=np.int64)[:max_tokens]
-    w13 = {e: synth.moe_expert_weights(cfg, "w13", e) for e in best}
-    w2 = {e: synth.moe_expert_weights(cfg, "w2", e) for e in best}
-    t0 = time.perf_counter()                                   # the oracle's w4_pack, beside the GPU's
-    packed13 = {e: oracle.w4_pack(w13[e]) for e in best}
-    packed2 = {e: oracle.w4_pack(w2[e]) for e in best}
-    pack_s = time.perf_counter() - t0
-    pack_n = sum(w13[e].size + w2[e].size for e in best)
-    del w13, w2
-    # the same forward repeated until about 10 s of host time (at most 8 runs)
-    runs, dt = 0, 0.0
-    while runs < 8 and dt < 10.0:
+    packed13, packed2, pack_s, pack_n = {}, {}, 0.0, 0
+    for e in range(cfg.E):
+        w13 = synth.moe_expert_weights(cfg, "w13", e)
+        w2 = synth.moe_expert_weights(cfg, "w2", e)
         t0 = time.perf_counter()
-        oracle.moe_forward(x, logits, s_x, lambda e: packed13[e], lambda e: packed2[e], cfg.act, s_a, cfg.out_f32,
-                           tokens=toks, E=cfg.E)
-        dt += time.perf_counter() - t0
-        runs += 1
+        packed13[e] = oracle.w4_pack(w13)
+        packed2[e] = oracle.w4_pack(w2)
+        pack_s += time.perf_counter() - t0
+        pack_n += w13.size + w2.size
+        del w13, w2
+    t0 = time.perf_counter()
+    oracle.moe_forward(x, logits, s_x, lambda e: packed13[e], lambda e: packed2[e], cfg.act, s_a, cfg.out_f32,
+                       E=cfg.E)
+    dt = time.perf_counter() - t0
     return {"oracle_w4_pack": {"weights": int(pack_n), "s": round(pack_s, 3),
                                "GB/s": round(pack_n * 3.5 / pack_s / 1e9, 3)},
-            "value": float(runs * len(toks) / dt), "unit": "tokens/s",
+            "value": float(cfg.T / dt), "unit": "tokens/s",
             "cores": int(max(1, blas_threads)), "host_cpus": len(os.sched_getaffinity(0)), "kind": "oracle",
-            "sample": f"{len(toks)} of {cfg.T} tokens (routed to experts {best[0]} and {best[1]}), "
-                      f"full oracle forward (fp64, int4 unpack, exact sums), {runs} runs, {dt:.2f} s"}
+            "sample": f"{cfg.T} of {cfg.T} tokens: the whole {cfg.name} layer (all {cfg.E} experts, fp64 oracle "
+                      f"forward with per-expert chunked int4 unpacking and exact sums), one run, {dt:.2f} s"}
 
 
 def bench_block_gemv(torch, W, dev, reps=16, iters=50):
@@ -227,6 +227,69 @@ def bench_kv_store(torch, W, dev, T=32, D=1024, slots_total=65536, iters=100):
     torch.cuda.synchronize()
     us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
     return {"us": round(us, 3), "tokens": T, "row_elements": D, "timed": f"{iters} calls in one HIP graph"}
+
+
+SWEEP_TOKENS = (32, 64, 65, 128, 256, 512, 1024)
+
+
+def token_sweep(torch, W, base, iters=20):
+    """The two grouped GEMMs of the Mixtral-shaped layer at batch sizes around the switch
+    from the streaming kernel (up to 64 tokens) to the tiled one: per T, each call's
+    average time over back-to-back launches, its HBM rate (touched experts' weights and
+    scales, activations in and out) and its matrix rate (routed rows only). The weights
+    are rotated over two copies so that they stream from HBM."""
+    import dataclasses
+    dev = torch.device("cuda:0")
+    s_x, s_a = static_scales(base.name)
+    w13b = bf16_dev(torch, synth.moe_weights(base, "w13"), dev)
+    w13, s13 = W.w4_pack(w13b, tiled=True)
+    del w13b
+    w2b = bf16_dev(torch, synth.moe_weights(base, "w2"), dev)
+    w2, s2 = W.w4_pack(w2b, tiled=True)
+    del w2b
+    W13, W2 = [w13, w13.clone()], [w2, w2.clone()]
+    H, I, E = base.H, base.I, base.E
+    st = torch.cuda.current_stream()
+    out = {}
+    for T in SWEEP_TOKENS:
+        cfg = dataclasses.replace(base, T=T)
+        x = bf16_dev(torch, synth.activations(dataclasses.replace(base, T=max(T, 32)))[:T], dev)
+        logits = torch.from_numpy(synth.router_logits(dataclasses.replace(base, T=max(T, 32)))[:T]).to(dev)
+        xq = torch.empty((T, H), dtype=torch.uint8, device=dev)
+        ro = W.route_outputs(T, E, dev)
+        W.moe_route_sort_quant(logits, x, s_x, out=ro, xq=xq)
+        a = torch.empty((2 * T, I), dtype=torch.uint8, device=dev)
+        y = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        ws2 = torch.empty(max(256, W.workspace_bytes(W.OP_GEMM2, T, H, I, E)), dtype=torch.uint8, device=dev)
+
+        def g1(i):
+            W.moe_gemm1_w4a8(xq, s_x, W13[i % 2], s13, ro["offsets"], ro["sorted_pair"], cfg.act, s_a, out=a)
+
+        def g2(i):
+            W.moe_gemm2_w4a8(a, s_a, W2[i % 2], s2, ro["offsets"], ro["pair_pos"], ro["weights"], "bf16", ws=ws2,
+                             out=y)
+        res = {}
+        for name, fn in (("gate_up", g1), ("down_combine", g2)):
+            for i in range(3):
+                fn(i)
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            ev[0].record(st)
+            for i in range(iters):
+                fn(i)
+            ev[1].record(st)
+            torch.cuda.synchronize()
+            res[name] = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+        counts = ro["counts"].cpu().numpy()
+        _, g1_bytes, touched = moe_bytes(cfg, counts)
+        g2_bytes = touched * (H * I // 2 + H * 4) + 2 * T * I + T * H * 2
+        out[str(T)] = {"kernel": "tiled" if W.moe_kernel(T) == W.KERNEL_TILED else "streaming",
+                       "gate_up_us": round(res["gate_up"], 2), "down_combine_us": round(res["down_combine"], 2),
+                       "gate_up_GB/s": round(g1_bytes / res["gate_up"] / 1e3, 1),
+                       "gate_up_TFLOP/s": round(gemm1_flops(cfg) / res["gate_up"] / 1e6, 1),
+                       "down_GB/s": round(g2_bytes / res["down_combine"] / 1e3, 1),
+                       "tokens_per_s_two_gemms": round(T / ((res["gate_up"] + res["down_combine"]) * 1e-6), 1)}
+    del W13, W2
+    return out
 
 
 def copy_bandwidth(torch, dev, nbytes=1 << 30, iters=10):
@@ -421,6 +484,15 @@ def main():
         result["prefill"] = {k: pf[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
                                                  "layer_mfma_frac", "calls_us", "roofline")}
         torch.cuda.empty_cache()
+    if args.workload == "mixtral_decode" and not args.no_grok_decode:
+        # the largest single-GPU decode layer: Grok-1-shaped, 2.42 GB of int4 weights per step
+        gd, _ = measure_layer(torch, W, synth.GROK_DECODE, args.steps, args.warmup)
+        result["grok_decode"] = {k: gd[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
+                                                     "layer_hbm_frac", "layer_bytes", "calls_us", "roofline")}
+        torch.cuda.empty_cache()
+    if args.workload == "mixtral_decode" and not args.no_token_sweep:
+        result["token_sweep"] = token_sweep(torch, W, synth.MIXTRAL_DECODE)
+        torch.cuda.empty_cache()
     if result["roofline"]["bound"] == "hbm":
         cb = copy_bandwidth(torch, dev)
         result["hbm_copy_ref"] = {"GB/s": round(cb, 1), "of_peak": round(cb / HBM_PEAK_GBS, 4),
@@ -437,7 +509,7 @@ def main():
         result["fp8_linear_w8a8"] = bench_fp8_linear(torch, W, dev)
         result["fp8_kv_cache_store"] = bench_kv_store(torch, W, dev)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, *static_scales(cfg.name), ids)
+        result["cpu_baseline"] = cpu_baseline(cfg, *static_scales(cfg.name))
     print(json.dumps(result), flush=True)
 
 

@@ -232,6 +232,14 @@ PREFILL_CASES = [
     # the largest expert count the calls accept: 600 rows over 256 experts, tiles of one to a few rows
     synth.custom_moe("pf_max_experts", T=300, H=128, I=128, E=256, w_cfg=308, x_cfg=308, out_f32=False,
                      logit_sigma=2.0),
+    # batches between decode and prefill (8 experts: 32 and 64 rows per expert on average)
+    synth.custom_moe("pf_mid_128", T=128, H=512, I=1024, E=8, act=synth.ACT_SILU, w_cfg=309, x_cfg=309,
+                     out_f32=False, logit_sigma=1.5),
+    synth.custom_moe("pf_mid_256", T=256, H=512, I=1024, E=8, act=synth.ACT_GELU_ERF, w_cfg=310, x_cfg=310,
+                     out_f32=False, logit_sigma=1.5),
+    # a small grid with a long reduction: the down projection split into 4 K-slices
+    synth.custom_moe("pf_split_k", T=96, H=256, I=4096, E=8, act=synth.ACT_SILU, w_cfg=311, x_cfg=311,
+                     out_f32=False, logit_sigma=1.5),
 ]
 
 

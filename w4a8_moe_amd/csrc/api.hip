@@ -41,10 +41,10 @@ size_t gemm1_ws(int32_t T, int32_t H, bool bf16_x) { return bf16_x ? round_up((s
 
 // gemm2's split-K partials: the same plan the launch uses.
 int gemm2_ksplit(int32_t T, int32_t H, int32_t I, int32_t E) {
-  if (!decode_fits(T)) return 1;
   MoeGemmParams p{};
   p.E = E; p.K = I; p.Nw = H; p.n_out = H; p.P = 2 * T;
-  plan_decode(p, false);
+  if (decode_fits(T)) plan_decode(p, false);
+  else plan_prefill(p, false);
   return p.ksplit;
 }
 
@@ -232,6 +232,7 @@ int32_t moe_gemm1_w4a8(const void* x, int32_t x_dtype, float s_x, const int32_t*
     plan_decode(p, true);
     launch_moe_decode(p, true, s);
   } else {
+    plan_prefill(p, true);
     launch_moe_prefill(p, true, s);
   }
   return launch_status();
@@ -268,6 +269,8 @@ int32_t moe_gemm2_w4a8(const uint8_t* a_fp8, float s_a, const int32_t* w2, const
     ksplit = p.ksplit;
     launch_moe_decode(p, false, s);
   } else {
+    plan_prefill(p, false);
+    ksplit = p.ksplit;
     launch_moe_prefill(p, false, s);
   }
   if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;

@@ -73,11 +73,13 @@ constexpr int kDecodeMaxTiles = 4;                // 16-row column tiles per exp
 constexpr int kDecodeLds = W4A8_DECODE_LDS_KB * 1024;
 
 bool decode_fits(int T);             // the streaming kernel handles T tokens
+int device_cus();                    // CUs of the current device (cached per device, thread-safe)
 void plan_decode(MoeGemmParams& p, bool gateup);
 void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 bool prefill_available();
 int prefill_token_blocks(int P, int E);   // 16-row token blocks per tile of the tiled kernel
+void plan_prefill(MoeGemmParams& p, bool gateup);   // split-K of the tiled down projection
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 // combine: out[t] = w0 * sum_s partial[s][pair_pos[2t]] + w1 * sum_s partial[s][pair_pos[2t+1]]

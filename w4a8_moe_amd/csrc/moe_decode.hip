@@ -23,6 +23,7 @@
 // instruction of a wave fetches one contiguous 1 KB tile (16 rows x 128 K), and a wave's
 // whole stream over K is contiguous.
 #include <algorithm>
+#include <atomic>
 
 #include "common.h"
 #include "kernels.h"
@@ -290,16 +291,18 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
 
 bool decode_fits(int T) { return T <= 16 * kDecodeMaxTiles; }
 
-// CUs of the current device (the streaming kernel holds two workgroups per CU).
-static int device_cus() {
-  static int cus[64] = {0};
+// CUs of the current device, looked up once per device. Each slot is an atomic, so calls
+// from several host threads are safe (every writer stores the same value).
+int device_cus() {
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    cus[dev] = (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0) ? n : 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return n;
 }
 
 // Fraction of the workgroup slots busy over the rounds that `units` workgroups take.

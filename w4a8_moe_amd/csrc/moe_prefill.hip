@@ -96,9 +96,13 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   // on XCD b % 8; each XCD gets a contiguous run of the tile order, and the order walks
   // bands of kGroupM M-tiles, all N-tiles of a band before the next band. The workgroups
   // resident on one XCD then share a few token tiles and a few weight tiles in its L2.
+  // With a split reduction (down projection of a small grid), the K-slice is the fastest
+  // index of that order.
   const int nblk = gridDim.x, b = blockIdx.x;
   const int q = nblk / 8, rr = nblk % 8, xcd = b % 8;
-  const int t = (xcd < rr ? xcd * (q + 1) : rr * (q + 1) + (xcd - rr) * q) + b / 8;
+  const int tk = (xcd < rr ? xcd * (q + 1) : rr * (q + 1) + (xcd - rr) * q) + b / 8;
+  const int slice = GATEUP ? 0 : tk % p.ksplit;
+  const int t = GATEUP ? tk : tk / p.ksplit;
   const int span = kGroupM * ntiles, band = t / span, rem = t % span;
   const int gm = min(kGroupM, mtiles_upper - band * kGroupM);
   const int mt = band * kGroupM + rem % gm, ntile = rem / gm;
@@ -152,18 +156,20 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 #pragma unroll
     for (int a = 0; a < 4; ++a) acc[bb][a] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const int steps = p.K / 128;
+  const int k0 = slice * p.kslice;                           // the slice's K range
+  const int steps = (min(p.K - k0, p.kslice)) / 128;
+  const uint32_t kb = (uint32_t)(k0 / 128);                 // its first k-step
   // an out-of-range offset stays out of range after adding k (offsets < 2^31, k < 2^30)
   uint4 tq[kTJ];
   auto load_tokens = [&](int s) {
 #pragma unroll
-    for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16s(tr, toff[j], (uint32_t)(s * 128));
+    for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s) * 128));
   };
   uint4 wc[4], wn[4];          // raw weights of steps s and s+1
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    wc[a] = pf_ld16s(wr, woff[a], 0);
-    wn[a] = pf_ld16s(wr, woff[a], kTileBytes);
+    wc[a] = pf_ld16s(wr, woff[a], kb * kTileBytes);
+    wn[a] = pf_ld16s(wr, woff[a], (kb + 1) * kTileBytes);
   }
   load_tokens(0);
   auto store_tokens = [&](uint8_t* T, int j) {
@@ -190,7 +196,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
       wc[a] = wn[a];
-      wn[a] = pf_ld16s(wr, woff[a], (uint32_t)((s + 2) * kTileBytes));
+      wn[a] = pf_ld16s(wr, woff[a], (uint32_t)((kb + s + 2) * kTileBytes));
     }
     // token blocks in order, each block's 16 MFMAs (4 K-parts x 4 weight blocks) together:
     // an accumulator's four MFMAs of the step are adjacent, which keeps every accumulator in
@@ -213,7 +219,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
       if ((bb & 1) == 0) {
         const int j = bb >> 1;
         store_tokens(Tn, j);                                               // step s+1
-        tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((s + 2) * 128));           // step s+2
+        tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s + 2) * 128));      // step s+2
       }
       __builtin_amdgcn_sched_barrier(0);
       if (bb + 1 < TB) {
@@ -272,7 +278,7 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
         }
       }
     } else {
-      float* prow = p.partial + r * p.n_out;
+      float* prow = p.partial + ((size_t)slice * p.P + r) * p.n_out;
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int nb = nbs[a];
@@ -298,13 +304,40 @@ int prefill_token_blocks(int P, int E) {
   return mean <= 64 ? 4 : (mean <= 128 ? 8 : 16);
 }
 
+// Split of the down projection's reduction. Gate|up needs the whole K (its epilogue forms
+// the activation). The down projection of a small grid (few M-tiles: batches of a few
+// hundred tokens) is split into K-slices of at least 8 k-steps until about two workgroups
+// per CU hold work, as long as the extra partial sums' round trip (8 bytes per row, channel
+// and slice) stays under a quarter of the weight bytes; the combine adds them in slice
+// order. Measured (Mixtral-shaped down + combine): 65 tokens 128 -> 91 us and 128 tokens
+// 128 -> 95 us with 4 slices; 512 tokens 194 -> 228 us with 4 slices, hence the limit.
+void plan_prefill(MoeGemmParams& p, bool gateup) {
+  p.ksplit = 1;
+  p.kslice = p.K;
+  if (gateup) return;
+  const int pm = 16 * prefill_token_blocks(p.P, p.E);
+  const int est_mtiles = std::max((p.P + pm - 1) / pm, std::min(p.E, p.P));   // M-tiles holding rows
+  const long tiles = (long)est_mtiles * ((p.Nw + kPN - 1) / kPN);
+  const long want = 2L * device_cus();
+  const int steps = p.K / 128;
+  const double weight_bytes = (double)std::min(p.E, p.P) * p.Nw * (p.K / 2);
+  const double slice_bytes = 8.0 * p.P * p.Nw;              // one more slice's partials, written and read
+  const int by_traffic = 1 + (int)(0.25 * weight_bytes / slice_bytes);
+  int ks = (int)std::min<long>((want + tiles - 1) / tiles, std::max(1, steps / 8));
+  ks = std::min(ks, by_traffic);
+  ks = std::max(1, std::min(ks, 16));
+  const int per = (steps + ks - 1) / ks;                    // k-steps per slice
+  p.kslice = per * 128;
+  p.ksplit = (steps + per - 1) / per;
+}
+
 template <int TB>
 static void launch_tb(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   constexpr int kPM = 16 * TB;
   // every expert's rows split into tiles of kPM; the count of tiles is at most P/kPM + E
   const int mtiles_upper = (p.P + kPM - 1) / kPM + p.E;
   const int ntiles = gateup ? (p.n_out + kPN / 2 - 1) / (kPN / 2) : (p.Nw + kPN - 1) / kPN;
-  const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles);
+  const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles * (gateup ? 1 : p.ksplit));
   const size_t lds = 2 * TB * 4096;
   if (!gateup)
     hipLaunchKernelGGL((moe_prefill_kernel<false, 0, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
