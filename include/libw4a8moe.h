@@ -80,6 +80,7 @@ extern "C" {
 #define W4A8_OP_BLOCK_LINEAR  5   /* args: M, N, K, - */
 #define W4A8_OP_TENSOR_QUANT  6   /* args: -, -, -, - */
 #define W4A8_OP_FP8_LINEAR    7   /* args: M, N, K, - */
+#define W4A8_OP_LAYER         8   /* moe_layer_w4a8; args: T, H, I, E */
 
 /* Size limits checked by every MoE call. */
 #define W4A8_MAX_EXPERTS 256
@@ -247,6 +248,27 @@ int32_t moe_gemm2_w4a8_noalloc(const uint8_t* a_fp8, float s_a,
                                int32_t T, int32_t H, int32_t I, int32_t E,
                                int32_t out_dtype, void* out, void* stream);
 size_t moe_gemm2_w4a8_noalloc_max_workspace(void);
+
+/*
+ * moe_layer_w4a8 -- the whole routed-expert layer in one call: moe_route_sort_quant,
+ * moe_gemm1_w4a8 and moe_gemm2_w4a8 on the same arguments, with every intermediate in the
+ * workspace (the computation of pages "ROCm: enable trillion-parameter MoE models with
+ * INT4-FP8 single node", INT4 MoE weights with FP8 compute and top-2 of 8 routing on the
+ * unquantized router, and "[AMD][Quantization] Add int4fp8_moe online quantization on
+ * ROCm", int4 weights upcast to FP8).
+ *
+ *   logits [T][E] fp32, x_bf16 [T][H] bf16, s_x, w13 / s_w13, w2 / s_w2, act, s_a,
+ *   out_dtype and out as in the three calls; out = the output of moe_gemm2_w4a8 after
+ *   those calls, byte for byte (the same launches, in the same order, on the stream).
+ * Requires what the three calls require. Workspace: w4a8_workspace_bytes(W4A8_OP_LAYER,
+ * T, H, I, E) (routing outputs, x codes, intermediate codes, partial sums).
+ */
+int32_t moe_layer_w4a8(const float* logits, const uint16_t* x_bf16, float s_x,
+                       const int32_t* w13, const float* s_w13,
+                       const int32_t* w2, const float* s_w2,
+                       int32_t T, int32_t H, int32_t I, int32_t E, int32_t act, float s_a,
+                       int32_t out_dtype, void* out,
+                       void* ws, size_t ws_bytes, void* stream);
 
 /*
  * fp8_block_quant -- block-FP8 quantization of a dense bf16 weight (the FP8_PB_WO

@@ -18,7 +18,7 @@ def L():
 def test_exports_every_declared_function(L):
     names = W.header_functions()
     assert set(names) == {"w4_pack", "w4_tile", "fp8_quant_static", "moe_route_sort", "moe_route_sort_quant", "moe_gemm1_w4a8", "moe_gemm2_w4a8",
-                          "moe_gemm2_w4a8_noalloc", "moe_gemm2_w4a8_noalloc_max_workspace",
+                          "moe_gemm2_w4a8_noalloc", "moe_gemm2_w4a8_noalloc_max_workspace", "moe_layer_w4a8",
                           "fp8_block_quant", "fp8_block_linear", "fp8_tensor_quant", "fp8_linear_w8a8",
                           "fp8_kv_cache_store",
                           "w4a8_workspace_bytes", "w4a8_status_str", "w4a8_moe_kernel"}
@@ -165,6 +165,30 @@ def test_gemm2_noalloc_validation(L):
     # 2 T H 4 bytes of partials at least: 4096 tokens x 6144 channels is 192 MiB
     assert W.workspace_bytes(W.OP_GEMM2, 4096, 6144, 32768, 8) > 32 << 20
     assert g(T=4096, H=6144, I=32768) == W.ERR_WORKSPACE
+
+
+def test_layer_validation(L):
+    """The one-call layer rejects bad arguments before any HIP call; its workspace holds at
+    least the routing outputs, x codes, intermediate codes and the down projection's sums."""
+    def g(T=32, H=256, I=512, E=8, act=W.ACT_SILU, s_x=0.5, s_a=0.5, dt=W.DT_BF16, out=A, ws=A, ws_bytes=None):
+        if ws_bytes is None:
+            ws_bytes = W.workspace_bytes(W.OP_LAYER, T, H, I, E)
+        return L.moe_layer_w4a8(A, A, s_x, A, A, A, A, T, H, I, E, act, s_a, dt, out, ws, ws_bytes, None)
+    assert g(I=384 + 64) == W.ERR_SHAPE
+    assert g(E=1) == W.ERR_SHAPE
+    assert g(act=7) == W.ERR_ARG
+    assert g(dt=W.DT_E4M3) == W.ERR_ARG
+    assert g(s_x=float("inf")) == W.ERR_ARG
+    assert g(s_a=-1.0) == W.ERR_ARG
+    assert g(out=None) == W.ERR_NULL
+    assert g(ws=None) == W.ERR_NULL
+    assert g(out=U) == W.ERR_ALIGN
+    assert g(T=0) == W.OK
+    for T, H, I, E in ((32, 256, 512, 8), (1, 4096, 14336, 8), (64, 6144, 32768, 8), (300, 256, 512, 4)):
+        need = W.workspace_bytes(W.OP_LAYER, T, H, I, E)
+        assert need >= 2 * T * (12 + I + 4 * H) + T * H
+        assert g(T=T, H=H, I=I, E=E, ws_bytes=need - 1) == W.ERR_WORKSPACE
+    assert W.workspace_bytes(W.OP_LAYER, 32, 256, 384 + 64, 8) == 0
 
 
 def test_block_validation(L):

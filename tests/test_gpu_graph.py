@@ -63,6 +63,38 @@ def test_layer_graph_replays_match_eager(cfg):
         assert t.equal(a, ref_a), f"replay {r}: intermediate differs from the eager step"
 
 
+@pytest.mark.parametrize("cfg", LAYERS, ids=[c.name for c in LAYERS])
+def test_one_call_layer_graph_replays_match_eager(cfg):
+    """moe_layer_w4a8 captured: replays over a workspace full of stale bytes give the eager
+    bytes."""
+    t = torch()
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    w13, s13 = W.w4_pack(bf16_dev(synth.moe_weights(cfg, "w13")), tiled=True)
+    w2, s2 = W.w4_pack(bf16_dev(synth.moe_weights(cfg, "w2")), tiled=True)
+    x = bf16_dev(synth.activations(cfg))
+    logits = f32_dev(synth.router_logits(cfg))
+    out = t.empty((T, H), dtype=t.bfloat16, device="cuda")
+    ws = t.empty(W.workspace_bytes(W.OP_LAYER, T, H, I, E), dtype=t.uint8, device="cuda")
+
+    def step():
+        W.moe_layer_w4a8(logits, x, 0.01, w13, s13, w2, s2, cfg.act, 0.05, "bf16", ws=ws, out=out)
+
+    step()
+    t.cuda.synchronize()
+    ref_out = out.clone()
+    g = t.cuda.CUDAGraph()
+    with t.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.fill_(float(r + 1)); ws.fill_(r + 3)
+        if r == 2:
+            step()
+        t.cuda.synchronize()
+        g.replay()
+        t.cuda.synchronize()
+        assert t.equal(out, ref_out), f"replay {r}: output differs from the eager call"
+
+
 @pytest.mark.parametrize("M", [1, 8])
 def test_fp8_linear_graph_replays_match_eager(M):
     t = torch()

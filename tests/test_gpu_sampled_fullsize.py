@@ -11,7 +11,8 @@ that end-to-end result. Sampled tokens include those whose rows sit at the first
 last rows of every expert segment and at tile edges; sampled output channels include
 the first and last ones and those at tile edges. As a separate check of the down call
 alone, the output also meets the bar against the oracle's down projection of the
-kernel's own codes.
+kernel's own codes. The one-call layer, moe_layer_w4a8, gives the same output bytes as
+the three calls.
 """
 import concurrent.futures as cf
 
@@ -91,7 +92,13 @@ def _run_sampled(cfg, n_tokens, n_out_ch=512):
     r = W.moe_route_sort(f32_dev(logits))
     a = W.moe_gemm1_w4a8(bf16_dev(x), s_x, gw["w13"][0], gw["w13"][1], r["offsets"], r["sorted_pair"], cfg.act, s_a)
     out = W.moe_gemm2_w4a8(a, s_a, gw["w2"][0], gw["w2"][1], r["offsets"], r["pair_pos"], r["weights"], "bf16")
+    # the one-call layer (what the benchmark times) gives the same bytes
+    out1 = W.moe_layer_w4a8(f32_dev(logits), bf16_dev(x), s_x, gw["w13"][0], gw["w13"][1], gw["w2"][0],
+                            gw["w2"][1], cfg.act, s_a, "bf16")
     torch().cuda.synchronize()
+    assert torch().equal(out1, out), "moe_layer_w4a8 differs from the three calls"
+    del out1
+    torch().cuda.empty_cache()
 
     ids, wts = oracle.route_top2(logits)
     counts, offsets, sp, pos = oracle.route_sort(ids, E)

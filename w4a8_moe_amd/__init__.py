@@ -21,7 +21,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_ARG, ERR
 ACT_SILU, ACT_GELU_ERF, ACT_GELU_TANH = 0, 1, 2
 DT_F32, DT_BF16, DT_E4M3 = 0, 1, 2
 OP_ROUTE_SORT, OP_GEMM1, OP_GEMM1_BF16, OP_GEMM2, OP_BLOCK_LINEAR = 1, 2, 3, 4, 5
-OP_TENSOR_QUANT, OP_FP8_LINEAR = 6, 7
+OP_TENSOR_QUANT, OP_FP8_LINEAR, OP_LAYER = 6, 7, 8
 
 _lock = threading.Lock()
 _lib = None
@@ -43,6 +43,8 @@ _SIGNATURES = {
     "moe_gemm2_w4a8": (_I32, [_P, _F32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "moe_gemm2_w4a8_noalloc": (_I32, [_P, _F32, _P, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _P, _P]),
     "moe_gemm2_w4a8_noalloc_max_workspace": (_SZ, []),
+    "moe_layer_w4a8": (_I32, [_P, _P, _F32, _P, _P, _P, _P, _I32, _I32, _I32, _I32, _I32, _F32, _I32, _P, _P, _SZ,
+                              _P]),
     "fp8_block_quant": (_I32, [_P, _I32, _I32, _P, _P, _P]),
     "fp8_block_linear": (_I32, [_P, _P, _P, _I32, _I32, _I32, _P, _P, _SZ, _P]),
     "fp8_tensor_quant": (_I32, [_P, _I64, _P, _P, _P, _SZ, _P]),
@@ -313,6 +315,35 @@ def moe_gemm2_w4a8_noalloc(a, s_a, w2, s_w2, offsets, pair_pos, topk_w, out_dtyp
 
 def noalloc_max_workspace():
     return int(lib().moe_gemm2_w4a8_noalloc_max_workspace())
+
+
+def moe_layer_w4a8(logits, x, s_x, w13, s_w13, w2, s_w2, act, s_a, out_dtype="bf16", ws=None, out=None):
+    """The whole layer in one library call: logits fp32 [T, E], x bf16 [T, H], w13 and w2
+    in the tiled layout -> out [T, H] (bf16 or fp32). ``ws`` (uint8, at least
+    workspace_bytes(OP_LAYER, T, H, I, E)) is allocated here when not given."""
+    torch = _torch()
+    T, H = x.shape
+    if w13.dim() != 4 or w2.dim() != 4:
+        raise ValueError("w13, w2: expected the tiled layout (w4_tile)")
+    E = w13.shape[0]
+    I = w13.shape[1] * 16 // 2
+    _need(logits, torch.float32, (T, E), "logits")
+    _need(x, torch.bfloat16, (T, H), "x")
+    _need(w13, torch.int32, (E, 2 * I // 16, H // 128, 256), "w13 (tiled)")
+    _need(s_w13, torch.float32, (E, 2 * I), "s_w13")
+    _need(w2, torch.int32, (E, H // 16, I // 128, 256), "w2 (tiled)")
+    _need(s_w2, torch.float32, (E, H), "s_w2")
+    dt = DT_BF16 if out_dtype in ("bf16", torch.bfloat16) else DT_F32
+    dev = x.device
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16 if dt == DT_BF16 else torch.float32, device=dev)
+    nws = workspace_bytes(OP_LAYER, T, H, I, E)
+    if ws is None or ws.numel() < nws:
+        ws = _workspace(nws, dev)
+    _check("moe_layer_w4a8", lib().moe_layer_w4a8(_ptr(logits), _ptr(x), float(s_x), _ptr(w13), _ptr(s_w13),
+                                                  _ptr(w2), _ptr(s_w2), T, H, I, E, int(act), float(s_a), dt,
+                                                  _ptr(out), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
 
 
 def fp8_block_quant(w):

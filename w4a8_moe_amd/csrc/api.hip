@@ -53,6 +53,30 @@ size_t gemm2_ws(int32_t T, int32_t H, int32_t I, int32_t E) {
   return round_up((size_t)gemm2_ksplit(T, H, I, E) * 2 * T * H * sizeof(float), 256);
 }
 
+// moe_layer_w4a8's workspace: the routing outputs, x codes, intermediate codes and the down
+// projection's partial sums, each at a 256-byte boundary.
+struct LayerWs {
+  size_t ids, tw, counts, offsets, sorted_pair, pair_pos, route, xq, a, partial, total;
+};
+
+LayerWs layer_ws(int32_t T, int32_t H, int32_t I, int32_t E) {
+  LayerWs w{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += round_up(bytes, 256); return at; };
+  w.ids = take((size_t)2 * T * sizeof(int32_t));
+  w.tw = take((size_t)2 * T * sizeof(float));
+  w.counts = take((size_t)E * sizeof(int32_t));
+  w.offsets = take((size_t)(E + 1) * sizeof(int32_t));
+  w.sorted_pair = take((size_t)2 * T * sizeof(int32_t));
+  w.pair_pos = take((size_t)2 * T * sizeof(int32_t));
+  w.route = take(route_workspace_bytes(T, E));
+  w.xq = take((size_t)T * H);
+  w.a = take((size_t)2 * T * I);
+  w.partial = take(gemm2_ws(T, H, I, E));
+  w.total = o;
+  return w;
+}
+
 // ---- the allocation-free variant's scratch: the down projection's split-K partials in a
 // file-scope device array, one copy per GPU for the life of the process. Its address on
 // each device comes from hipGetSymbolAddress, taken once per device with that device
@@ -109,6 +133,9 @@ size_t w4a8_workspace_bytes(int32_t op, int32_t T_or_M, int32_t H_or_N, int32_t 
     case W4A8_OP_GEMM2:
       if (check_moe_shape(T_or_M, H_or_N, I_or_K, E) != W4A8_OK) return 0;
       return gemm2_ws(T_or_M, H_or_N, I_or_K, E);
+    case W4A8_OP_LAYER:
+      if (check_moe_shape(T_or_M, H_or_N, I_or_K, E) != W4A8_OK) return 0;
+      return T_or_M == 0 ? 0 : layer_ws(T_or_M, H_or_N, I_or_K, E).total;
     case W4A8_OP_BLOCK_LINEAR:
       return 0;
     case W4A8_OP_TENSOR_QUANT:
@@ -298,6 +325,66 @@ int32_t moe_gemm2_w4a8_noalloc(const uint8_t* a_fp8, float s_a, const int32_t* w
 }
 
 size_t moe_gemm2_w4a8_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int32_t moe_layer_w4a8(const float* logits, const uint16_t* x_bf16, float s_x, const int32_t* w13,
+                       const float* s_w13, const int32_t* w2, const float* s_w2, int32_t T, int32_t H, int32_t I,
+                       int32_t E, int32_t act, float s_a, int32_t out_dtype, void* out, void* ws, size_t ws_bytes,
+                       void* stream) {
+  int32_t st = check_moe_shape(T, H, I, E);
+  if (st != W4A8_OK) return st;
+  if (act != W4A8_ACT_SILU && act != W4A8_ACT_GELU_ERF && act != W4A8_ACT_GELU_TANH) return W4A8_ERR_ARG;
+  if (out_dtype != W4A8_DT_BF16 && out_dtype != W4A8_DT_F32) return W4A8_ERR_ARG;
+  if (!good_scale(s_x) || !good_scale(s_a)) return W4A8_ERR_ARG;
+  if (T == 0) return W4A8_OK;
+  if (!logits || !x_bf16 || !w13 || !s_w13 || !w2 || !s_w2 || !out || !ws) return W4A8_ERR_NULL;
+  if (!aligned16(logits) || !aligned16(x_bf16) || !aligned16(w13) || !aligned16(s_w13) || !aligned16(w2) ||
+      !aligned16(s_w2) || !aligned16(out) || !aligned16(ws))
+    return W4A8_ERR_ALIGN;
+  const LayerWs w = layer_ws(T, H, I, E);
+  if (ws_bytes < w.total) return W4A8_ERR_WORKSPACE;
+  const bool decode = decode_fits(T);
+  if (!decode && !prefill_available()) return W4A8_ERR_UNSUPPORTED;
+
+  hipStream_t s = as_stream(stream);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  int32_t* ids = reinterpret_cast<int32_t*>(base + w.ids);
+  float* tw = reinterpret_cast<float*>(base + w.tw);
+  int32_t* counts = reinterpret_cast<int32_t*>(base + w.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(base + w.offsets);
+  int32_t* sorted_pair = reinterpret_cast<int32_t*>(base + w.sorted_pair);
+  int32_t* pair_pos = reinterpret_cast<int32_t*>(base + w.pair_pos);
+  uint8_t* xq = base + w.xq;
+  uint8_t* a = base + w.a;
+  float* partial = reinterpret_cast<float*>(base + w.partial);
+  launch_route_sort(logits, T, E, ids, tw, counts, offsets, sorted_pair, pair_pos, base + w.route, s, x_bf16,
+                    (int64_t)T * H, s_x, xq);
+  if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;
+
+  MoeGemmParams g{};
+  g.act = xq; g.w = w13; g.w_scale = s_w13; g.offsets = offsets; g.sorted_pair = sorted_pair;
+  g.E = E; g.K = H; g.Nw = 2 * I; g.n_out = I; g.P = 2 * T;
+  g.s_act = s_x; g.act_fn = act; g.s_a = s_a; g.inv_s_a = 1.0f / s_a; g.a_out = a; g.dbg = nullptr;
+  MoeGemmParams d{};
+  d.act = a; d.w = w2; d.w_scale = s_w2; d.offsets = offsets; d.sorted_pair = nullptr;
+  d.E = E; d.K = I; d.Nw = H; d.n_out = H; d.P = 2 * T;
+  d.s_act = s_a; d.partial = partial;
+  if (decode) {
+    plan_decode(g, true);
+    launch_moe_decode(g, true, s);
+    if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;
+    plan_decode(d, false);
+    launch_moe_decode(d, false, s);
+  } else {
+    plan_prefill(g, true);
+    launch_moe_prefill(g, true, s);
+    if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;
+    plan_prefill(d, false);
+    launch_moe_prefill(d, false, s);
+  }
+  if (launch_status() != W4A8_OK) return W4A8_ERR_HIP;
+  launch_combine(partial, d.ksplit, 2 * T, H, pair_pos, tw, T, out_dtype == W4A8_DT_BF16, out, s);
+  return launch_status();
+}
 
 int32_t fp8_block_quant(const uint16_t* w_bf16, int32_t N, int32_t K, uint8_t* w_e4m3, float* scales,
                         void* stream) {

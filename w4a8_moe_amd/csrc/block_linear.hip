@@ -67,17 +67,6 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
   const int KB = K >> 7;
-  // ---- stage x: unit (kb, j, g, m) = 8 bf16 = x[m][kb*128 + g*32 + j*8 .. +8], stored at
-  //      ((kb*4 + j)*4 + g)*M + m, so lane (m, g) of MFMA j reads 16 contiguous bytes.
-  const int units = M * (K >> 3);
-  for (int u = tid; u < units; u += kWaves * kWave) {
-    const int m = u / (K >> 3), c8 = u - m * (K >> 3);       // 8-element chunk of row m
-    const int kb = c8 >> 4, within = c8 & 15;                // 16 chunks per 128-K block
-    const int g = within >> 2, j = within & 3;
-    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + c8 * 8);
-    *reinterpret_cast<uint4*>(lds + ((((kb * 4 + j) * 4 + g) * M + m) << 4)) = v;
-  }
-  __syncthreads();
   const int rb = min(blockIdx.x * RB + wave / kBlSplit, N / 16 - 1);   // 16-row block
   const bool rb_ok = blockIdx.x * RB + wave / kBlSplit < N / 16;      // else: no K blocks, no store
   const int part_k = wave % kBlSplit;
@@ -88,8 +77,7 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
   // this wave's 128-K blocks [kb_begin, kb_end)
   const int per = (KB + kBlSplit - 1) / kBlSplit;
   const int kb_begin = min(KB, part_k * per), kb_end = rb_ok ? min(KB, kb_begin + per) : kb_begin;
-
-  v4f acc = {0.f, 0.f, 0.f, 0.f};
+  // the first weight blocks are requested before x is staged (they do not depend on it)
   uint4 q0[kBlDepth], q1[kBlDepth];
 #pragma unroll
   for (int d = 0; d < kBlDepth; ++d)
@@ -97,6 +85,19 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
       q0[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128);
       q1[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128 + 16);
     }
+  // ---- stage x: unit (kb, j, g, m) = 8 bf16 = x[m][kb*128 + g*32 + j*8 .. +8], stored at
+  //      ((kb*4 + j)*4 + g)*M + m, so lane (m, g) of MFMA j reads 16 contiguous bytes.
+  const int units = M * (K >> 3);
+  for (int u = tid; u < units; u += kWaves * kWave) {
+    const int m = u / (K >> 3), c8 = u - m * (K >> 3);       // 8-element chunk of row m
+    const int kb = c8 >> 4, within = c8 & 15;                // 16 chunks per 128-K block
+    const int gg = within >> 2, j = within & 3;
+    const uint4 v = *reinterpret_cast<const uint4*>(x + (size_t)m * K + c8 * 8);
+    *reinterpret_cast<uint4*>(lds + ((((kb * 4 + j) * 4 + gg) * M + m) << 4)) = v;
+  }
+  __syncthreads();
+
+  v4f acc = {0.f, 0.f, 0.f, 0.f};
   for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kBlDepth) {
 #pragma unroll
     for (int d = 0; d < kBlDepth; ++d) {
