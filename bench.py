@@ -2,9 +2,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
-A step is one forward of the layer over one batch of synthetic tokens:
-moe_route_sort_quant (routing and x -> E4M3 in one call), moe_gemm1_w4a8,
-moe_gemm2_w4a8 (down + combine); four consecutive steps are captured in one HIP graph,
+A step is one forward of the layer over one batch of synthetic tokens: one moe_layer_w4a8
+call (the launches of moe_route_sort_quant, moe_gemm1_w4a8 and moe_gemm2_w4a8: routing and
+x -> E4M3, gate|up, down + combine; checked byte-equal to those three calls); four
+consecutive steps are captured in one HIP graph,
 as a model's decode graph holds its consecutive layers, and exactly K steps are timed. Inputs
 (packed weights, scales, x, logits) are resident in HBM before the timed region. The
 packed weights are rotated over several copies when one copy would fit in the 256 MB
@@ -28,6 +29,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense OCP-FP8 MFMA, published
+FP16_PEAK_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA, published
 METRIC = "MoE layer tokens/s + % HBM peak (decode T=32), % fp8 MFMA peak (prefill)"
 ACT_NAMES = {synth.ACT_SILU: "silu", synth.ACT_GELU_ERF: "gelu_erf", synth.ACT_GELU_TANH: "gelu_tanh"}
 
@@ -358,8 +360,18 @@ def measure_layer(torch, W, cfg, steps, warmup):
         W.moe_gemm2_w4a8(a, s_a, W2[i % copies], s2, ro["offsets"], ro["pair_pos"], ro["weights"], od, ws=ws2,
                          out=out)
 
+    wsl = torch.empty(max(256, W.workspace_bytes(W.OP_LAYER, T, H, I, E)), dtype=torch.uint8, device=dev)
+    out1 = torch.empty_like(out)
+
     def step(i):
-        route_quant(); gemm1(i); gemm2(i)
+        W.moe_layer_w4a8(logits, x, s_x, W13[i % copies], s13, W2[i % copies], s2, cfg.act, s_a, od, ws=wsl,
+                         out=out1)
+
+    # the one call and the three calls it stands for give the same bytes
+    route_quant(); gemm1(0); gemm2(0); step(0)
+    torch.cuda.synchronize()
+    if not torch.equal(out, out1):
+        raise RuntimeError("moe_layer_w4a8 differs from the three calls")
 
     # eager reference step, then captured HIP graphs (launch overhead of the Python binding
     # stays out of the timed region): per weight copy, one of a single step and one of
@@ -367,7 +379,7 @@ def measure_layer(torch, W, cfg, steps, warmup):
     # decode graph holds its consecutive layers; every replay must match the eager step
     step(0)
     torch.cuda.synchronize()
-    ref_out = out.clone()
+    ref_out = out1.clone()
     counts = ro["counts"].cpu().numpy()
     ids = ro["ids"].cpu().numpy()
     graphs1, graphsN = [], []
@@ -382,10 +394,10 @@ def measure_layer(torch, W, cfg, steps, warmup):
         graphs1[i % copies].replay()
     torch.cuda.synchronize()
     for g in (graphs1[0], graphsN[0]):
-        out.zero_()
+        out1.zero_()
         g.replay()
         torch.cuda.synchronize()
-        if not torch.equal(out, ref_out):
+        if not torch.equal(out1, ref_out):
             raise RuntimeError("graph replay differs from the eager step")
 
     # ---- timed region: exactly K steps (graphs of STEPS_PER_GRAPH steps, single-step
@@ -419,19 +431,25 @@ def measure_layer(torch, W, cfg, steps, warmup):
         return ev0.elapsed_time(ev1) * 1e3 / n
 
     per_call = {"route_sort_quant": per_launch_us(lambda i: route_quant()),
-                "gemm1": per_launch_us(gemm1), "gemm2_combine": per_launch_us(gemm2)}
+                "gemm1": per_launch_us(gemm1), "gemm2_combine": per_launch_us(gemm2),
+                "moe_layer_w4a8": per_launch_us(step)}
     layer_bytes, gemm1_bytes, touched = moe_bytes(cfg, counts)
     layer_us = ms_per_step * 1e3
     tiled = W.moe_kernel(T) == W.KERNEL_TILED
     if tiled:
         # many tokens per expert: the tiled kernel is bound by the fp8 matrix cores
+        # the products run on the 16-bit matrix instruction (exact E4M3 x int4 values in fp16),
+        # so the kernel's roofline is the fp16 dense peak; the fp8 peak's fraction is context
         tf = gemm1_flops(cfg) / (per_call["gemm1"] * 1e-6) / 1e12
-        roofline = {"kernel": "moe_gemm1_w4a8 (moe_prefill_kernel<gate|up>)", "bound": "mfma",
-                    "achieved": round(tf, 1), "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / FP8_PEAK_TFLOPS, 4), "traffic": counter_traffic(cfg.name),
-                    "flops_per_launch": gemm1_flops(cfg), "bytes_per_launch": int(gemm1_bytes)}
+        roofline = {"kernel": "moe_gemm1_w4a8 (moe_prefill_kernel<gate|up>, fp16 MFMA)", "bound": "mfma",
+                    "achieved": round(tf, 1), "peak": FP16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / FP16_PEAK_TFLOPS, 4), "traffic": counter_traffic(cfg.name),
+                    "flops_per_launch": gemm1_flops(cfg), "bytes_per_launch": int(gemm1_bytes),
+                    "frac_of_fp8_peak": round(tf / FP8_PEAK_TFLOPS, 4)}
         layer_flops = 2 * gemm1_flops(cfg) * 0.75         # gate|up + down (half the width of gate|up)
-        layer_frac = {"layer_mfma_frac": round(layer_flops / (layer_us * 1e-6) / 1e12 / FP8_PEAK_TFLOPS, 4)}
+        layer_tf = layer_flops / (layer_us * 1e-6) / 1e12
+        layer_frac = {"layer_mfma_frac": round(layer_tf / FP16_PEAK_TFLOPS, 4),
+                      "layer_fp8_peak_frac": round(layer_tf / FP8_PEAK_TFLOPS, 4)}
     else:
         g1_gbs = gemm1_bytes / per_call["gemm1"] / 1e3
         roofline = {"kernel": "moe_gemm1_w4a8 (moe_decode_kernel<gate|up>)", "bound": "hbm",

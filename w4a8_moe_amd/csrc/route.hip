@@ -83,7 +83,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_small_kernel(
   int q0, q1;
   wave_ranks(valid, r.i0, r.i1, E, wt, q0, q1);
   __syncthreads();
-  if (t == 0) {
+  if (E <= kWave) {
+    // wave 0, lane e: expert e's count, then an inclusive scan over the lanes
+    if (t < kWave) {
+      int c = 0;
+      if (t < E)
+        for (int w = 0; w < kRouteWaves; ++w) c += wt[w * E + t];
+      int incl = c;
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d);
+        if (t >= d) incl += v;
+      }
+      if (t < E) {
+        off[t] = incl - c;
+        counts[t] = c;
+        offsets[t] = incl - c;
+      }
+      if (t == E - 1) {
+        off[E] = incl;
+        offsets[E] = incl;
+      }
+    }
+  } else if (t == 0) {
     int run = 0;
     for (int e = 0; e < E; ++e) {
       off[e] = run;
