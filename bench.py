@@ -65,7 +65,8 @@ def bf16_dev(torch, bits, dev):
 
 STEPS_PER_GRAPH = 4      # consecutive layer steps captured in one HIP graph
 
-COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_prefill": "moe_prefill_grok_T32768.json"}
+COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_decode": "moe_decode_grok_T32.json",
+                 "grok_prefill": "moe_prefill_grok_T32768.json"}
 
 
 def sources_sha256(paths):
