@@ -339,6 +339,10 @@ static double plan_down(MoeGemmParams& p, int wmax, long experts, long slots) {
   return best;
 }
 
+// Four column tiles (33 to 64 tokens) take 4-wave workgroups: that kernel needs ~180 registers
+// per lane, so a CU holds 8 of its waves, as two workgroups of 4 rather than one of 8, which
+// keeps the two-per-CU slot count the plans assume. Mixtral-shaped gate|up at 40, 48, 64
+// tokens: 106 -> 98, 114 -> 103, 121 -> 111 us; down at 48 tokens 57 -> 49 us.
 void plan_decode(MoeGemmParams& p, bool gateup) {
   // an expert never holds more rows than there are tokens (its two slots differ)
   const int T = p.P / 2;
@@ -358,6 +362,7 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     double best = -1.0;
     for (int w : {8, 7, 4}) {
       if (w > kDecodeWaves) continue;
+      if (p.max_tiles >= 4 && w != 4) continue;             // four column tiles: see above
       const int groups = (p.n_out + 16 * w - 1) / (16 * w);
       const double fill = round_fill((long)groups * experts, slots);
       if (fill > best + 1e-9) {
@@ -372,7 +377,7 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     // us; a single round keeps 8: Mixtral shape 50.0 us, 58.6 with 6).
     const long experts = std::min(p.E, 2 * T);
     const long slots = 2L * device_cus();
-    const double fill = plan_down(p, kDecodeWaves, experts, slots);
+    const double fill = plan_down(p, p.max_tiles >= 4 ? 4 : kDecodeWaves, experts, slots);
     if ((long)p.groups * p.ksplit * experts > slots && p.waves > 6) {
       MoeGemmParams q = p;
       if (plan_down(q, std::min(6, kDecodeWaves), experts, slots) >= fill - 0.02) {
