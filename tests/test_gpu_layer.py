@@ -30,6 +30,9 @@ CASES = [
                      logit_sigma=0.5),
     synth.custom_moe("fl_max_experts", T=24, H=128, I=128, E=256, w_cfg=508, x_cfg=508, out_f32=False,
                      logit_sigma=2.0),
+    # the fewest tokens that take four column tiles (4-wave workgroups), and the most, over 256 experts
+    synth.custom_moe("fl_33", T=33, H=384, I=768, E=4, act=synth.ACT_GELU_ERF, w_cfg=511, x_cfg=511, out_f32=False),
+    synth.custom_moe("fl_max_experts_64", T=64, H=128, I=256, E=256, w_cfg=512, x_cfg=512, logit_sigma=2.0),
     # above 64 tokens: the routing, the tiled gate|up and down launches in sequence
     synth.custom_moe("fl_sequential", T=100, H=256, I=512, E=8, act=synth.ACT_GELU_ERF, w_cfg=509, x_cfg=509,
                      out_f32=False),
