@@ -143,6 +143,28 @@ def cpu_baseline(cfg, s_x, s_a):
                       f"forward with per-expert chunked int4 unpacking and exact sums), one run, {dt:.2f} s"}
 
 
+def graph_call_us(torch, fn, iters):
+    """Average GPU time of fn(i), i < iters, captured back to back in one graph and replayed
+    between two HIP events on the current stream (the library launches on it)."""
+    for i in range(5):
+        fn(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(iters):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(st)
+    g.replay()
+    ev[1].record(st)
+    torch.cuda.synchronize()
+    del g
+    return ev[0].elapsed_time(ev[1]) * 1e3 / iters
+
+
 def bench_block_gemv(torch, W, dev, reps=16, iters=50):
     """block-FP8 GEMV at the projection shapes; weights rotated over `reps` copies."""
     out = {}
@@ -153,16 +175,7 @@ def bench_block_gemv(torch, W, dev, reps=16, iters=50):
         qs = [q.clone() for _ in range(reps)]
         x = bf16_dev(torch, synth.block_activations(cfg), dev)
         y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
-        for i in range(5):
-            W.fp8_block_linear(x, qs[i % reps], S, out=y)
-        st = torch.cuda.current_stream()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(st)
-        for i in range(iters):
-            W.fp8_block_linear(x, qs[i % reps], S, out=y)
-        ev[1].record(st)
-        torch.cuda.synchronize()
-        us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+        us = graph_call_us(torch, lambda i: W.fp8_block_linear(x, qs[i % reps], S, out=y), iters)
         nbytes = cfg.N * cfg.K + S.numel() * 4 + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2
         out[cfg.name] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
@@ -185,16 +198,9 @@ def bench_fp8_linear(torch, W, dev, reps=16, iters=50):
         qs = [q.clone() for _ in range(reps)]
         x = bf16_dev(torch, synth.block_activations(cfg), dev)
         y = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device=dev)
-        for i in range(5):
-            W.fp8_linear_w8a8(x, s_x, qs[i % reps], s_w, out=y)
-        st = torch.cuda.current_stream()
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(st)
-        for i in range(iters):
-            W.fp8_linear_w8a8(x, s_x, qs[i % reps], s_w, out=y)
-        ev[1].record(st)
-        torch.cuda.synchronize()
-        us = ev[0].elapsed_time(ev[1]) * 1e3 / iters
+        ws = torch.empty(max(256, W.workspace_bytes(W.OP_FP8_LINEAR, cfg.M, cfg.N, cfg.K, 0)), dtype=torch.uint8,
+                         device=dev)
+        us = graph_call_us(torch, lambda i: W.fp8_linear_w8a8(x, s_x, qs[i % reps], s_w, out=y, ws=ws), iters)
         nbytes = cfg.N * cfg.K + cfg.M * cfg.K * 2 + cfg.M * cfg.N * 2     # weights, bf16 x in, bf16 y out
         out[cfg.name] = {"us": round(us, 3), "GB/s": round(nbytes / us / 1e3, 1),
                          "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
@@ -416,20 +422,13 @@ def measure_layer(torch, W, cfg, steps, warmup):
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / steps
 
-    # ---- per-call duration: back-to-back launches of one call between two HIP events on
-    #      the stream the library launches on
-    st = torch.cuda.current_stream()
+    # ---- per-call duration: one call's launches back to back in a graph, between two HIP
+    #      events on the stream the library launches on
 
     def per_launch_us(fn, n=max(20, steps)):
-        for i in range(3):
-            fn(i)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record(st)
-        for i in range(n):
-            fn(i)
-        ev1.record(st)
-        torch.cuda.synchronize()
-        return ev0.elapsed_time(ev1) * 1e3 / n
+        # n calls captured back to back in one graph (so a short call is timed on the GPU, not
+        # behind the Python binding's launch cost), replayed between two events on the stream
+        return graph_call_us(torch, fn, n)
 
     per_call = {"route_sort_quant": per_launch_us(lambda i: route_quant()),
                 "gemm1": per_launch_us(gemm1), "gemm2_combine": per_launch_us(gemm2),
