@@ -56,7 +56,8 @@ __device__ __forceinline__ v4f mfma_bf16_16x16x32(v8bf a, v8bf b, v4f c) {
 // sums each instruction's products with about 14 bits of precision below the largest
 // product of the instruction (measured on MI355X: 256 + 127 * 2^-9 comes out as
 // 256.234375; random blocks up to 1.4e-4 of the sum of |products|), while its 16-bit
-// MFMAs return exact fp32 sums for these operands. Against the oracle's exact sums, that
+// MFMAs add these operands' exact products in fp32, with no error beyond fp32 rounding
+// (probe on the same blocks). Against the oracle's exact sums, the fp8 instruction's
 // error moves requantized codes and bf16 outputs across their rounding boundaries far
 // more often than the method's output tolerance allows. An E4M3 value and an int4 code are
 // both exact in fp16, so both grouped GEMMs multiply them on the fp16 MFMA (16x16x32),

@@ -6,10 +6,10 @@
 // page "[AMD][Quantization] Add int4fp8_moe online quantization on ROCm"): every product
 // is an E4M3 activation times an int4 weight code, summed in fp32; the per-channel and
 // static scales are applied in the epilogue. The products run on the fp16 MFMA
-// (16x16x32), whose sums of these exact values are exact (common.h: the fp8 MFMA's are
-// not, and its error breaks the output tolerance): int4 codes are widened to exact fp16
-// by exponent placement, E4M3 codes by the hardware conversion (those facing a weight's
-// high nibble divided by 16, exact).
+// (16x16x32), which forms them exactly and adds them in fp32 (common.h: the fp8 MFMA's
+// sums are less precise, and their error breaks the output tolerance): int4 codes are
+// widened to exact fp16 by exponent placement, E4M3 codes by the hardware conversion
+// (those facing a weight's high nibble divided by 16, exact).
 //
 // Tile. A workgroup computes TB blocks of 16 sorted rows (tokens of one expert; 64, 128
 // or 256 rows, chosen by the rows per expert) x 256 weight rows, K in steps of 128, with
