@@ -240,6 +240,10 @@ PREFILL_CASES = [
     # a small grid with a long reduction: the down projection split into 4 K-slices
     synth.custom_moe("pf_split_k", T=96, H=256, I=4096, E=8, act=synth.ACT_SILU, w_cfg=311, x_cfg=311,
                      out_f32=False, logit_sigma=1.5),
+    # odd k-step counts (3 for gate|up, 9 for down) through the two-step register ring of the
+    # 32-row tiles: the ring's last pass is half empty
+    synth.custom_moe("pf_odd_steps", T=80, H=384, I=1152, E=8, act=synth.ACT_GELU_ERF, w_cfg=312, x_cfg=312,
+                     out_f32=False, logit_sigma=1.5),
 ]
 
 
@@ -273,13 +277,13 @@ def test_moe_prefill_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-@pytest.mark.parametrize("T", [20, 130, 600])
-def test_integer_case_gate_up_bit_exact(T):
+@pytest.mark.parametrize("T,E", [(20, 4), (66, 8), (100, 4), (130, 4), (600, 4)])
+def test_integer_case_gate_up_bit_exact(T, E):
     """Integer x and w, max |w| = 7 per row, s_x = 1: fp32 accumulation is exact in any
     order, so gate|up must equal the integer product exactly (20 tokens: the streaming
-    kernel; 130 and 600: the tiled kernel with 64- and 256-row tiles)."""
+    kernel; then the tiled kernel with 32-, 64-, 128- and 256-row tiles)."""
     rng = np.random.default_rng(77 + T)
-    H, I, E = 384, 256, 4
+    H, I = 384, 256
     xi = rng.integers(-16, 17, size=(T, H))
     w13i = rng.integers(-7, 8, size=(E, 2 * I, H))
     w13i[:, :, 3] = 7

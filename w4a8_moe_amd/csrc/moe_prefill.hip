@@ -11,8 +11,8 @@
 // widened to exact fp16 by exponent placement, E4M3 codes by the hardware conversion
 // (those facing a weight's high nibble divided by 16, exact).
 //
-// Tile. A workgroup computes TB blocks of 16 sorted rows (tokens of one expert; 64, 128
-// or 256 rows, chosen by the rows per expert) x 256 weight rows, K in steps of 128, with
+// Tile. A workgroup computes TB blocks of 16 sorted rows (tokens of one expert; 32, 64,
+// 128 or 256 rows, chosen by the rows per expert) x 256 weight rows, K in steps of 128, with
 // 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against all TB token blocks, so
 // its int4 codes go from global memory straight into its own registers, are widened there
 // and used as MFMA operands without an LDS round trip. For gate|up the 64 rows are 32
@@ -22,12 +22,20 @@
 // staging chunks to fp16 once, and the waves read finished MFMA operands (1 KB per token
 // block and K-part, lane l's 16 bytes at 16 l: no bank conflicts on either side).
 //
-// Pipeline, per k-step s (one barrier each): widen the step's 16 weight words (4 blocks x
-// 4 MFMAs of K = 32) and issue the weight loads of step s+2; then walk the token blocks,
-// the next block's operands read ahead, storing the tokens of step s+1 (loaded one step
-// earlier) into the other LDS buffer and issuing the token loads of step s+2 on the way.
-// Loads past the last k-step read in-bounds data or zeros and are never used, so the
-// loop has no branches.
+// Pipeline of the 128- and 256-row tiles, per k-step s (one barrier each): widen the
+// step's 16 weight words (4 blocks x 4 MFMAs of K = 32) and issue the weight loads of step
+// s+2; then walk the token blocks, the next block's operands read ahead, storing the tokens
+// of step s+1 (loaded one step earlier) into the other LDS buffer and issuing the token
+// loads of step s+2 on the way. Loads past the last k-step read in-bounds data or zeros and
+// are never used, so the loop has no branches. (The compiler moves a step's fresh weight
+// loads into the ring by copies at the end of the step, which waits for them: in effect the
+// weights run one step ahead, which the long steps of these tiles cover.)
+//
+// The 32- and 64-row tiles have short steps (32 or 64 MFMAs per wave), so they keep their
+// loads R steps ahead in register rings without copies (the loop body unrolled by R, each
+// step's slot fixed), walk the K-parts in the outer loop and widen the next part's weights
+// while the current part's MFMAs run. Each accumulator sees its MFMAs in the same order in
+// both pipelines, so the two give the same bits.
 //
 // Measured on MI355X (Grok-1-shaped prefill, 256-row tiles, rocprofv3 counters): the matrix
 // cores are busy 54.7% (gate|up) and 60.0% (down) of the cycles, at 2.30 and 2.19 GHz; the
@@ -82,7 +90,7 @@ __device__ __forceinline__ int tok_slot(int i, int g, int h) { return 16 * g + (
 
 // TB: token blocks of 16 rows per tile. ACT: the gated activation (gate|up only), a template
 // parameter so that each instance carries the code of one activation in its epilogue.
-template <bool GATEUP, int ACT, int TB>
+template <bool GATEUP, int ACT, int TB, int R>
 __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles) {
   constexpr int kPM = 16 * TB;                       // sorted rows per tile
   constexpr int kTJ = kPM * 8 / kPThreads;           // 16-byte token chunks per thread and k-step
@@ -161,74 +169,153 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   const int steps = (min(p.K - k0, p.kslice)) / 128;
   const uint32_t kb = (uint32_t)(k0 / 128);                 // its first k-step
   // an out-of-range offset stays out of range after adding k (offsets < 2^31, k < 2^30)
-  uint4 tq[kTJ];
-  auto load_tokens = [&](int s) {
-#pragma unroll
-    for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s) * 128));
+  auto store_tokens = [&](uint8_t* T, int j, const uint4& q) {
+    *reinterpret_cast<v8h*>(T + tdst[j]) = e4m3x8_to_f16(q.x, q.y);
+    *reinterpret_cast<v8h*>(T + tdst[j] + 1024) = e4m3x8_to_f16(q.z, q.w);
   };
-  uint4 wc[4], wn[4];          // raw weights of steps s and s+1
-#pragma unroll
-  for (int a = 0; a < 4; ++a) {
-    wc[a] = pf_ld16s(wr, woff[a], kb * kTileBytes);
-    wn[a] = pf_ld16s(wr, woff[a], (kb + 1) * kTileBytes);
-  }
-  load_tokens(0);
-  auto store_tokens = [&](uint8_t* T, int j) {
-    *reinterpret_cast<v8h*>(T + tdst[j]) = e4m3x8_to_f16(tq[j].x, tq[j].y);
-    *reinterpret_cast<v8h*>(T + tdst[j] + 1024) = e4m3x8_to_f16(tq[j].z, tq[j].w);
-  };
-#pragma unroll
-  for (int j = 0; j < kTJ; ++j) store_tokens(lds, j);
-  load_tokens(1);
-  lds_barrier();
-
   // the two nibble masks of the widening live in registers (one 3-input bit op per mask)
   uint32_t mlo = 0x0F0F0F0Fu, mhi = 0xF0F0F0F0u;
   asm volatile("" : "+v"(mlo), "+v"(mhi));
-  for (int s = 0; s < steps; ++s) {
-    const uint8_t* Tc = lds + (s & 1) * kTokBytes;
-    uint8_t* Tn = lds + ((s & 1) ^ 1) * kTokBytes;
-    // this step's weight operands: word m of block a -> K 32 g + 8 m .. +8 of its rows
-    v8h A[4][4];
+  if constexpr (R == 0) {
+    uint4 tq[kTJ];
+    auto load_tokens = [&](int s) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int a = 0; a < 4; ++a) A[m][a] = int4x8_to_f16(word4(wc[a], m), mlo, mhi);
+      for (int j = 0; j < kTJ; ++j) tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s) * 128));
+    };
+    uint4 wc[4], wn[4];          // raw weights of steps s and s+1
 #pragma unroll
     for (int a = 0; a < 4; ++a) {
-      wc[a] = wn[a];
-      wn[a] = pf_ld16s(wr, woff[a], (uint32_t)((kb + s + 2) * kTileBytes));
+      wc[a] = pf_ld16s(wr, woff[a], kb * kTileBytes);
+      wn[a] = pf_ld16s(wr, woff[a], (kb + 1) * kTileBytes);
     }
-    // token blocks in order, each block's 16 MFMAs (4 K-parts x 4 weight blocks) together:
-    // an accumulator's four MFMAs of the step are adjacent, which keeps every accumulator in
-    // place (spread over the step, the register allocator rotates them through copies)
-    v8h Bc[4];
+    load_tokens(0);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) Bc[m] = *reinterpret_cast<const v8h*>(Tc + m * 1024 + rdl);
+    for (int j = 0; j < kTJ; ++j) store_tokens(lds, j, tq[j]);
+    load_tokens(1);
+    lds_barrier();
+
+    for (int s = 0; s < steps; ++s) {
+      const uint8_t* Tc = lds + (s & 1) * kTokBytes;
+      uint8_t* Tn = lds + ((s & 1) ^ 1) * kTokBytes;
+      // this step's weight operands: word m of block a -> K 32 g + 8 m .. +8 of its rows
+      v8h A[4][4];
 #pragma unroll
-    for (int bb = 0; bb < TB; ++bb) {
-      v8h Bn[4];
-      if (bb + 1 < TB) {
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int m = 0; m < 4; ++m) Bn[m] = *reinterpret_cast<const v8h*>(Tc + ((bb + 1) * 4 + m) * 1024 + rdl);
+        for (int a = 0; a < 4; ++a) A[m][a] = int4x8_to_f16(word4(wc[a], m), mlo, mhi);
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        wc[a] = wn[a];
+        wn[a] = pf_ld16s(wr, woff[a], (uint32_t)((kb + s + 2) * kTileBytes));
+      }
+      // token blocks in order, each block's 16 MFMAs (4 K-parts x 4 weight blocks) together:
+      // an accumulator's four MFMAs of the step are adjacent, which keeps every accumulator in
+      // place (spread over the step, the register allocator rotates them through copies)
+      v8h Bc[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) Bc[m] = *reinterpret_cast<const v8h*>(Tc + m * 1024 + rdl);
+#pragma unroll
+      for (int bb = 0; bb < TB; ++bb) {
+        v8h Bn[4];
+        if (bb + 1 < TB) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) Bn[m] = *reinterpret_cast<const v8h*>(Tc + ((bb + 1) * 4 + m) * 1024 + rdl);
+        }
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_f16(A[m][a], Bc[m], acc[bb][a]);
+        }
+        if ((bb & 1) == 0) {
+          const int j = bb >> 1;
+          store_tokens(Tn, j, tq[j]);                                        // step s+1
+          tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s + 2) * 128));      // step s+2
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (bb + 1 < TB) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) Bc[m] = Bn[m];
+        }
+      }
+      lds_barrier();
+    }
+  } else {
+    // Small tiles: a k-step is short (TB * 16 MFMAs per wave), so the loads run R k-steps
+    // ahead, in register rings with one fixed slot per step of an R-step loop body (a ring
+    // rotated by copies would wait for each refill at the copy). Weights of step u sit in
+    // wq[u % R]; tokens of step u in tq[u % R], stored to LDS during step u - 1. The weights
+    // are widened one K-part at a time, the next part's while this part's MFMAs run. A body
+    // past the last k-step still moves its ring (in-bounds or zero loads, never used) and
+    // meets its barrier, and skips the arithmetic.
+    // The prologue stages step 0's tokens, then issues the loads in the order one pass of
+    // the loop body issues them (weights of a step, then the tokens one step later), so the
+    // loop header sees the same loads in flight from either side and its waits stay precise.
+    uint4 wq[R][4], tq[R][kTJ];
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) tq[0][j] = pf_ld16s(tr, toff[j], kb * 128);
+#pragma unroll
+    for (int j = 0; j < kTJ; ++j) store_tokens(lds, j, tq[0][j]);
+#pragma unroll
+    for (int d = 0; d < R; ++d) {
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        wq[d][a] = pf_ld16s(wr, woff[a], (kb + d) * kTileBytes);
+        __builtin_amdgcn_sched_barrier(0);                // keep the issue order
       }
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-#pragma unroll
-        for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_f16(A[m][a], Bc[m], acc[bb][a]);
-      }
-      if ((bb & 1) == 0) {
-        const int j = bb >> 1;
-        store_tokens(Tn, j);                                               // step s+1
-        tq[j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s + 2) * 128));      // step s+2
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (bb + 1 < TB) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) Bc[m] = Bn[m];
+      for (int j = 0; j < kTJ; ++j) {
+        tq[(d + 1) % R][j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + d + 1) * 128));
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     lds_barrier();
+    for (int s0 = 0; s0 < steps; s0 += R) {
+#pragma unroll
+      for (int u = 0; u < R; ++u) {
+        const int s = s0 + u;
+        const uint8_t* Tc = lds + (s & 1) * kTokBytes;
+        uint8_t* Tn = lds + ((s & 1) ^ 1) * kTokBytes;
+        const int un = (u + 1) % R;                          // ring slot of step s + 1
+        if (s < steps) {
+          v8h Ac[4], Bc[TB];
+#pragma unroll
+          for (int a = 0; a < 4; ++a) Ac[a] = int4x8_to_f16(word4(wq[u][a], 0), mlo, mhi);
+#pragma unroll
+          for (int bb = 0; bb < TB; ++bb) Bc[bb] = *reinterpret_cast<const v8h*>(Tc + (bb * 4) * 1024 + rdl);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            v8h An[4], Bn[TB];
+            if (m + 1 < 4) {
+#pragma unroll
+              for (int a = 0; a < 4; ++a) An[a] = int4x8_to_f16(word4(wq[u][a], m + 1), mlo, mhi);
+#pragma unroll
+              for (int bb = 0; bb < TB; ++bb)
+                Bn[bb] = *reinterpret_cast<const v8h*>(Tc + (bb * 4 + m + 1) * 1024 + rdl);
+            }
+#pragma unroll
+            for (int bb = 0; bb < TB; ++bb)
+#pragma unroll
+              for (int a = 0; a < 4; ++a) acc[bb][a] = mfma_f16(Ac[a], Bc[bb], acc[bb][a]);
+            if (m + 1 < 4) {
+#pragma unroll
+              for (int a = 0; a < 4; ++a) Ac[a] = An[a];
+#pragma unroll
+              for (int bb = 0; bb < TB; ++bb) Bc[bb] = Bn[bb];
+            }
+          }
+        }
+        // refill: weights of step s + R into this step's slot; tokens of step s + 1 to LDS,
+        // then step s + 1 + R into their slot
+#pragma unroll
+        for (int a = 0; a < 4; ++a) wq[u][a] = pf_ld16s(wr, woff[a], (uint32_t)((kb + s + R) * kTileBytes));
+#pragma unroll
+        for (int j = 0; j < kTJ; ++j) {
+          store_tokens(Tn, j, tq[un][j]);
+          tq[un][j] = pf_ld16s(tr, toff[j], (uint32_t)((kb + s + 1 + R) * 128));
+        }
+        lds_barrier();
+      }
+    }
   }
 
   // ---- epilogue: lane holds weight rows 4g..4g+3 of each block, token column i. Every
@@ -293,16 +380,18 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 
 bool prefill_available() { return true; }
 
-// Token blocks per tile: the smallest of 4, 8, 16 that holds the mean rows per expert with
-// rows (P / E), so that an expert's weights are read by as few M-tiles as possible without
-// running the matrix cores on padding rows.
+// Token blocks per tile: the smallest of 2, 4, 8, 16 that holds the mean rows per expert
+// (P / E), so that an expert's weights are read by as few M-tiles as possible without
+// running the matrix cores on padding rows. Measured, Mixtral-shaped gate|up at 65 and 128
+// tokens (16 and 32 rows per expert): 143.6 -> 123.2 us and 170.3 -> 128.0 us with 32-row
+// instead of 64-row tiles (each with its register ring).
 int prefill_token_blocks(int P, int E) {
 #ifdef W4A8_PREFILL_TB
   (void)P; (void)E;
   return W4A8_PREFILL_TB;
 #endif
   const int mean = (P + E - 1) / E;
-  return mean <= 64 ? 4 : (mean <= 128 ? 8 : 16);
+  return mean <= 32 ? 2 : (mean <= 64 ? 4 : (mean <= 128 ? 8 : 16));
 }
 
 // Split of the down projection's reduction. Gate|up needs the whole K (its epilogue forms
@@ -332,31 +421,44 @@ void plan_prefill(MoeGemmParams& p, bool gateup) {
   p.ksplit = (steps + per - 1) / per;
 }
 
+// Depth of the register rings of the 32- and 64-row tiles (0: the copy pipeline of the
+// larger tiles). Measured, Mixtral-shaped gate|up at 65 tokens: 139.3 us with 32-row tiles
+// and no ring, 128.6 with a ring of 4, 123.2 with 2; with 64-row tiles (256 tokens) 194.5 ->
+// 187.1 us with a ring of 2 (3: 191.1, 4: 194.5). 128-row tiles were slower with a ring
+// (512 tokens: 417 -> 439-486 us) and keep the copies.
+#ifndef W4A8_PREFILL_RING2
+#define W4A8_PREFILL_RING2 2
+#endif
+#ifndef W4A8_PREFILL_RING4
+#define W4A8_PREFILL_RING4 2
+#endif
 template <int TB>
 static void launch_tb(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   constexpr int kPM = 16 * TB;
+  constexpr int R = TB == 2 ? W4A8_PREFILL_RING2 : (TB == 4 ? W4A8_PREFILL_RING4 : 0);
   // every expert's rows split into tiles of kPM; the count of tiles is at most P/kPM + E
   const int mtiles_upper = (p.P + kPM - 1) / kPM + p.E;
   const int ntiles = gateup ? (p.n_out + kPN / 2 - 1) / (kPN / 2) : (p.Nw + kPN - 1) / kPN;
   const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles * (gateup ? 1 : p.ksplit));
   const size_t lds = 2 * TB * 4096;
   if (!gateup)
-    hipLaunchKernelGGL((moe_prefill_kernel<false, 0, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+    hipLaunchKernelGGL((moe_prefill_kernel<false, 0, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
                        ntiles);
   else if (p.act_fn == 0)
-    hipLaunchKernelGGL((moe_prefill_kernel<true, 0, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 0, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
                        ntiles);
   else if (p.act_fn == 1)
-    hipLaunchKernelGGL((moe_prefill_kernel<true, 1, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 1, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
                        ntiles);
   else
-    hipLaunchKernelGGL((moe_prefill_kernel<true, 2, TB>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
+    hipLaunchKernelGGL((moe_prefill_kernel<true, 2, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
                        ntiles);
 }
 
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   const int tb = prefill_token_blocks(p.P, p.E);
-  if (tb == 4) launch_tb<4>(p, gateup, st);
+  if (tb == 2) launch_tb<2>(p, gateup, st);
+  else if (tb == 4) launch_tb<4>(p, gateup, st);
   else if (tb == 8) launch_tb<8>(p, gateup, st);
   else launch_tb<16>(p, gateup, st);
 }
