@@ -424,8 +424,10 @@ void plan_prefill(MoeGemmParams& p, bool gateup) {
 // Depth of the register rings of the 32- and 64-row tiles (0: the copy pipeline of the
 // larger tiles). Measured, Mixtral-shaped gate|up at 65 tokens: 139.3 us with 32-row tiles
 // and no ring, 128.6 with a ring of 4, 123.2 with 2; with 64-row tiles (256 tokens) 194.5 ->
-// 187.1 us with a ring of 2 (3: 191.1, 4: 194.5). 128-row tiles were slower with a ring
-// (512 tokens: 417 -> 439-486 us) and keep the copies.
+// 187.1 us with a ring of 2 (3: 191.1, 4: 194.5). 128-row tiles were slower with a ring in
+// either loop order (512 tokens: 408 us with the copies; K-parts outer 439-486 us, token
+// blocks outer 464 / 484 / 486 us for rings of 2 / 3 / 4) and keep the copies; 256-row
+// tiles have no registers left for one.
 #ifndef W4A8_PREFILL_RING2
 #define W4A8_PREFILL_RING2 2
 #endif
