@@ -213,8 +213,9 @@ def test_moe_layer_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-# Token counts above 64 take the tiled kernel: 256-row tiles over each expert's segment
-# (ragged last tiles, empty experts), 128-channel gate|up tiles, 256-channel down tiles.
+# Token counts above 64 take the tiled kernel: tiles of 32 to 256 rows (by the mean rows per
+# expert) over each expert's segment (ragged last tiles, empty experts), 128-channel gate|up
+# tiles, 256-channel down tiles.
 PREFILL_CASES = [
     synth.custom_moe("pf_small", T=96, H=256, I=512, E=4, w_cfg=301, x_cfg=301),
     # the fewest tokens that take the tiled kernel (64 take the streaming one)
