@@ -352,7 +352,7 @@ const char* w4a8_status_str(int32_t status);
 
 /* Which kernel the MoE GEMM calls use for T tokens (T >= 0): W4A8_KERNEL_STREAM, the
  * weight-streaming kernel for few tokens per expert (bound by HBM), or
- * W4A8_KERNEL_TILED, the tiled kernel for many tokens per expert (32-, 64-, 128- or 256-row
+ * W4A8_KERNEL_TILED, the tiled kernel for many tokens per expert (32-, 64- or 256-row
  * tiles x 256 weight rows, bound by the 16-bit matrix cores). Both take the same exact
  * products, so results of either meet the same accuracy contract. */
 #define W4A8_KERNEL_STREAM 0

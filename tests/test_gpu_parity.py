@@ -213,8 +213,8 @@ def test_moe_layer_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-# Token counts above 64 take the tiled kernel: tiles of 32 to 256 rows (by the mean rows per
-# expert) over each expert's segment (ragged last tiles, empty experts), 128-channel gate|up
+# Token counts above 64 take the tiled kernel: tiles of 32, 64 or 256 rows (by the mean rows
+# per expert) over each expert's segment (ragged last tiles, empty experts), 128-channel gate|up
 # tiles, 256-channel down tiles.
 PREFILL_CASES = [
     synth.custom_moe("pf_small", T=96, H=256, I=512, E=4, w_cfg=301, x_cfg=301),
@@ -244,6 +244,9 @@ PREFILL_CASES = [
     # odd k-step counts (3 for gate|up, 9 for down) through the two-step register ring of the
     # 32-row tiles: the ring's last pass is half empty
     synth.custom_moe("pf_odd_steps", T=80, H=384, I=1152, E=8, act=synth.ACT_GELU_ERF, w_cfg=312, x_cfg=312,
+                     out_f32=False, logit_sigma=1.5),
+    # enough rows per expert (about 1600) for the 256-row tiles
+    synth.custom_moe("pf_big_tiles", T=3200, H=256, I=512, E=4, act=synth.ACT_SILU, w_cfg=313, x_cfg=313,
                      out_f32=False, logit_sigma=1.5),
 ]
 
@@ -278,11 +281,11 @@ def test_moe_prefill_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-@pytest.mark.parametrize("T,E", [(20, 4), (66, 8), (100, 4), (130, 4), (600, 4)])
+@pytest.mark.parametrize("T,E", [(20, 4), (66, 8), (100, 4), (600, 4), (3200, 2)])
 def test_integer_case_gate_up_bit_exact(T, E):
     """Integer x and w, max |w| = 7 per row, s_x = 1: fp32 accumulation is exact in any
     order, so gate|up must equal the integer product exactly (20 tokens: the streaming
-    kernel; then the tiled kernel with 32-, 64-, 128- and 256-row tiles)."""
+    kernel; then the tiled kernel with 32-, 64- (two cases) and 256-row tiles)."""
     rng = np.random.default_rng(77 + T)
     H, I = 384, 256
     xi = rng.integers(-16, 17, size=(T, H))

@@ -11,8 +11,8 @@
 // widened to exact fp16 by exponent placement, E4M3 codes by the hardware conversion
 // (those facing a weight's high nibble divided by 16, exact).
 //
-// Tile. A workgroup computes TB blocks of 16 sorted rows (tokens of one expert; 32, 64,
-// 128 or 256 rows, chosen by the rows per expert) x 256 weight rows, K in steps of 128, with
+// Tile. A workgroup computes TB blocks of 16 sorted rows (tokens of one expert; 32, 64 or
+// 256 rows, chosen by the rows per expert) x 256 weight rows, K in steps of 128, with
 // 4 waves. Wave w owns 64 weight rows (4 blocks of 16) against all TB token blocks, so
 // its int4 codes go from global memory straight into its own registers, are widened there
 // and used as MFMA operands without an LDS round trip. For gate|up the 64 rows are 32
@@ -22,7 +22,7 @@
 // staging chunks to fp16 once, and the waves read finished MFMA operands (1 KB per token
 // block and K-part, lane l's 16 bytes at 16 l: no bank conflicts on either side).
 //
-// Pipeline of the 128- and 256-row tiles, per k-step s (one barrier each): widen the
+// Pipeline of the 256-row tiles, per k-step s (one barrier each): widen the
 // step's 16 weight words (4 blocks x 4 MFMAs of K = 32) and issue the weight loads of step
 // s+2; then walk the token blocks, the next block's operands read ahead, storing the tokens
 // of step s+1 (loaded one step earlier) into the other LDS buffer and issuing the token
@@ -380,18 +380,31 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
 
 bool prefill_available() { return true; }
 
-// Token blocks per tile: the smallest of 2, 4, 8, 16 that holds the mean rows per expert
-// (P / E), so that an expert's weights are read by as few M-tiles as possible without
-// running the matrix cores on padding rows. Measured, Mixtral-shaped gate|up at 65 and 128
-// tokens (16 and 32 rows per expert): 143.6 -> 123.2 us and 170.3 -> 128.0 us with 32-row
-// instead of 64-row tiles (each with its register ring).
+// Token blocks per tile, by the mean rows per expert (P / E): 32-row tiles up to 48 rows,
+// 64-row tiles up to 1536, 256-row tiles above. The 32- and 64-row tiles run two
+// workgroups per CU with register rings, and up to about a thousand rows per expert that
+// outweighs reading each weight tile once per 64 rows instead of once per 256; the 256-row
+// tiles win once an expert holds many of them (their weights then come from the caches).
+// 128-row tiles were never the fastest. Measured gate|up / down, us (same box):
+//   Mixtral-shaped   96 tokens: 32-row 143 / 79,   64-row 140 / 81
+//                   192 tokens: 32-row 168 / 98,   64-row 189 / 104
+//                   256 tokens: 32-row 208 / 110,  64-row 199 / 114
+//                   512 tokens: 64-row 295 / 155,  128-row 408 / 206
+//                  1024 tokens: 64-row 483 / 282,  256-row 716 / 324
+//                  4096 tokens: 64-row 1708 / 859, 256-row 1884 / 976
+//                  8192 tokens: 64-row 3428 / 1699, 256-row 3557 / 1718
+//                 16384 tokens: 64-row 6814 / 3371, 256-row 6562 / 3088
+//   Grok-1-shaped   2048 tokens: 64-row 3090 / 1500, 256-row 3608 / 1843
+//                   4096 tokens: 64-row 5949 / 2934, 256-row 6066 / 2921
+//                   8192 tokens: 64-row 11435 / 5652, 256-row 11117 / 5179
+//                  32768 tokens: 64-row 44428 / 21947, 256-row 39594 / 19223
 int prefill_token_blocks(int P, int E) {
 #ifdef W4A8_PREFILL_TB
   (void)P; (void)E;
-  return W4A8_PREFILL_TB;
+  return W4A8_PREFILL_TB;   // 2, 4 or 16
 #endif
   const int mean = (P + E - 1) / E;
-  return mean <= 32 ? 2 : (mean <= 64 ? 4 : (mean <= 128 ? 8 : 16));
+  return mean <= 48 ? 2 : (mean <= 1536 ? 4 : 16);
 }
 
 // Split of the down projection's reduction. Gate|up needs the whole K (its epilogue forms
@@ -461,7 +474,6 @@ void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   const int tb = prefill_token_blocks(p.P, p.E);
   if (tb == 2) launch_tb<2>(p, gateup, st);
   else if (tb == 4) launch_tb<4>(p, gateup, st);
-  else if (tb == 8) launch_tb<8>(p, gateup, st);
   else launch_tb<16>(p, gateup, st);
 }
 
