@@ -50,7 +50,6 @@ namespace w4a8 {
 
 constexpr int kPN = 256;          // weight rows per tile
 constexpr int kPThreads = 256;    // 4 waves, 64 weight rows each
-constexpr int kGroupM = 4;        // M-tiles per band of the tile order
 constexpr uint32_t kPOutOfRange = 0x80000000u;   // past every buffer (all are < 2^31 bytes)
 
 // per-lane offset plus a wave-uniform one (the step), added by the load itself
@@ -91,7 +90,8 @@ __device__ __forceinline__ int tok_slot(int i, int g, int h) { return 16 * g + (
 // TB: token blocks of 16 rows per tile. ACT: the gated activation (gate|up only), a template
 // parameter so that each instance carries the code of one activation in its epilogue.
 template <bool GATEUP, int ACT, int TB, int R>
-__global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles) {
+__global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams p, int mtiles_upper, int ntiles,
+                                                                   int groupm, int chunk) {
   constexpr int kPM = 16 * TB;                       // sorted rows per tile
   constexpr int kTJ = kPM * 8 / kPThreads;           // 16-byte token chunks per thread and k-step
   constexpr int kTokBytes = TB * 4096;               // blocks of 16 rows x 128 K, fp16
@@ -101,20 +101,22 @@ __global__ __launch_bounds__(kPThreads, 1) void moe_prefill_kernel(MoeGemmParams
   const int wave = __builtin_amdgcn_readfirstlane(wave_id());
   const int i = lane & 15, g = lane >> 4;
 
-  // Tile order. Workgroups are dispatched round-robin over the 8 XCDs, so workgroup b runs
-  // on XCD b % 8; each XCD gets a contiguous run of the tile order, and the order walks
-  // bands of kGroupM M-tiles, all N-tiles of a band before the next band. The workgroups
-  // resident on one XCD then share a few token tiles and a few weight tiles in its L2.
-  // With a split reduction (down projection of a small grid), the K-slice is the fastest
-  // index of that order.
-  const int nblk = gridDim.x, b = blockIdx.x;
-  const int q = nblk / 8, rr = nblk % 8, xcd = b % 8;
-  const int tk = (xcd < rr ? xcd * (q + 1) : rr * (q + 1) + (xcd - rr) * q) + b / 8;
+  // Tile order. The order walks bands of groupm M-tiles, all N-tiles of a band before the
+  // next band (with a split reduction, the K-slice is the fastest index). Workgroups are
+  // dispatched round-robin over the 8 XCDs (workgroup b on XCD b % 8), and XCD x takes
+  // chunks x, x + 8, x + 16, ... of chunk consecutive tiles of the order (chunk: about the
+  // workgroups one XCD holds at once): the workgroups resident on an XCD share a few token
+  // and weight tiles in its L2, and the empty tiles at the end of the order (the M-tile
+  // count is an upper bound) are spread over all XCDs. The grid is a whole number of 8
+  // chunks; tiles past the order's end exit.
+  const int b = blockIdx.x, xcd = b % 8, kx = b / 8;
+  const int tk = ((kx / chunk) * 8 + xcd) * chunk + kx % chunk;
+  if (tk >= mtiles_upper * ntiles * (GATEUP ? 1 : p.ksplit)) return;
   const int slice = GATEUP ? 0 : tk % p.ksplit;
   const int t = GATEUP ? tk : tk / p.ksplit;
-  const int span = kGroupM * ntiles, band = t / span, rem = t % span;
-  const int gm = min(kGroupM, mtiles_upper - band * kGroupM);
-  const int mt = band * kGroupM + rem % gm, ntile = rem / gm;
+  const int span = groupm * ntiles, band = t / span, rem = t % span;
+  const int gm = min(groupm, mtiles_upper - band * groupm);
+  const int mt = band * groupm + rem % gm, ntile = rem / gm;
   TileOrigin o;
   if (!locate_mtile(p.offsets, p.E, kPM, mt, o)) return;
   const int rows = min(kPM, o.cnt - o.m0);                  // valid sorted rows in this tile
@@ -441,6 +443,15 @@ void plan_prefill(MoeGemmParams& p, bool gateup) {
 // either loop order (512 tokens: 408 us with the copies; K-parts outer 439-486 us, token
 // blocks outer 464 / 484 / 486 us for rings of 2 / 3 / 4) and keep the copies; 256-row
 // tiles have no registers left for one.
+#ifndef W4A8_PREFILL_GROUPM_SMALL
+#define W4A8_PREFILL_GROUPM_SMALL 16
+#endif
+#ifndef W4A8_PREFILL_GROUPM_LARGE
+#define W4A8_PREFILL_GROUPM_LARGE 4
+#endif
+#ifndef W4A8_PREFILL_CHUNK_MUL
+#define W4A8_PREFILL_CHUNK_MUL 1
+#endif
 #ifndef W4A8_PREFILL_RING2
 #define W4A8_PREFILL_RING2 2
 #endif
@@ -454,20 +465,25 @@ static void launch_tb(const MoeGemmParams& p, bool gateup, hipStream_t st) {
   // every expert's rows split into tiles of kPM; the count of tiles is at most P/kPM + E
   const int mtiles_upper = (p.P + kPM - 1) / kPM + p.E;
   const int ntiles = gateup ? (p.n_out + kPN / 2 - 1) / (kPN / 2) : (p.Nw + kPN - 1) / kPN;
-  const unsigned grid = (unsigned)((size_t)mtiles_upper * ntiles * (gateup ? 1 : p.ksplit));
+  const size_t tiles = (size_t)mtiles_upper * ntiles * (gateup ? 1 : p.ksplit);
+  // workgroups one XCD holds at once: its CUs times the workgroups per CU (two for the
+  // 32- and 64-row tiles, one for the 256-row tiles)
+  const int chunk = std::max(1, device_cus() / 8) * (TB <= 4 ? 2 : 1) * W4A8_PREFILL_CHUNK_MUL;
+  const int groupm = TB <= 4 ? W4A8_PREFILL_GROUPM_SMALL : W4A8_PREFILL_GROUPM_LARGE;
+  const unsigned grid = (unsigned)((tiles + 8 * (size_t)chunk - 1) / (8 * (size_t)chunk) * 8 * chunk);
   const size_t lds = 2 * TB * 4096;
   if (!gateup)
     hipLaunchKernelGGL((moe_prefill_kernel<false, 0, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
-                       ntiles);
+                       ntiles, groupm, chunk);
   else if (p.act_fn == 0)
     hipLaunchKernelGGL((moe_prefill_kernel<true, 0, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
-                       ntiles);
+                       ntiles, groupm, chunk);
   else if (p.act_fn == 1)
     hipLaunchKernelGGL((moe_prefill_kernel<true, 1, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
-                       ntiles);
+                       ntiles, groupm, chunk);
   else
     hipLaunchKernelGGL((moe_prefill_kernel<true, 2, TB, R>), dim3(grid), dim3(kPThreads), lds, st, p, mtiles_upper,
-                       ntiles);
+                       ntiles, groupm, chunk);
 }
 
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
