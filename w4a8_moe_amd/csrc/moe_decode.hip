@@ -289,7 +289,16 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   }
 }
 
-bool decode_fits(int T) { return T <= 16 * kDecodeMaxTiles; }
+// The streaming kernel takes up to 52 tokens (at most four 16-row column tiles per
+// expert); the tiled kernel is faster from about 56. Measured gate|up / down, us, streaming
+// against tiled: Mixtral-shaped 48 tokens 105.2 / 51.3 against 107.8 / 58.5, 52 tokens
+// 99.0 / 51.1 against 98.8 / 61.6, 56 tokens 109.7 / 61.4 against 96.7 / 62.2, 64 tokens
+// 114.3 / 65.3 against 96.7 / 63.3; Grok-1-shaped 48 tokens 311.3 / 176.2 against 306.8 /
+// 179.0, 64 tokens 347.6 / 193.7 against 291.1 / 181.9 (one GPU's 8-way share of Grok-1
+// keeps preferring streaming up to 56 tokens: 82.9 against 90.1 us for both GEMMs).
+constexpr int kStreamMaxTokens = 52;
+static_assert(kStreamMaxTokens <= 16 * kDecodeMaxTiles, "an expert's rows fit the column tiles");
+bool decode_fits(int T) { return T <= kStreamMaxTokens; }
 
 // CUs of the current device, looked up once per device. Each slot is an atomic, so calls
 // from several host threads are safe (every writer stores the same value).
@@ -339,7 +348,7 @@ static double plan_down(MoeGemmParams& p, int wmax, long experts, long slots) {
   return best;
 }
 
-// Four column tiles (33 to 64 tokens) take 4-wave workgroups: that kernel needs ~180 registers
+// Four column tiles (33 to 52 tokens) take 4-wave workgroups: that kernel needs ~180 registers
 // per lane, so a CU holds 8 of its waves, as two workgroups of 4 rather than one of 8, which
 // keeps the two-per-CU slot count the plans assume. Mixtral-shaped gate|up at 40, 48, 64
 // tokens: 106 -> 98, 114 -> 103, 121 -> 111 us; down at 48 tokens 57 -> 49 us.
