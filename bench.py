@@ -47,8 +47,10 @@ def parse():
                     help="with the default decode workload, skip the prefill layer's line")
     ap.add_argument("--no-grok-decode", action="store_true",
                     help="with the default decode workload, skip the Grok-1-shaped decode layer's line")
+    ap.add_argument("--no-tp8", action="store_true",
+                    help="with the default decode workload, skip one GPU's 8-way share of the Grok-1 layer")
     ap.add_argument("--no-token-sweep", action="store_true",
-                    help="with the default decode workload, skip the 64..1024-token sweep of the two GEMMs")
+                    help="with the default decode workload, skip the 32..1024-token sweep of the two GEMMs")
     ap.add_argument("--copy-ref", action="store_true",
                     help="also run a 1 GiB device-to-device copy (a known-size reference for HBM counters)")
     return ap.parse_args()
@@ -443,8 +445,8 @@ def measure_layer(torch, W, cfg, steps, warmup):
     layer_us = ms_per_step * 1e3
     tiled = W.moe_kernel(T) == W.KERNEL_TILED
     if tiled:
-        # many tokens per expert: the tiled kernel is bound by the fp8 matrix cores
-        # the products run on the 16-bit matrix instruction (exact E4M3 x int4 values in fp16),
+        # many tokens per expert: the tiled kernel is bound by the matrix cores; the products
+        # run on the 16-bit matrix instruction (exact E4M3 x int4 values in fp16),
         # so the kernel's roofline is the fp16 dense peak; the fp8 peak's fraction is context
         tf = gemm1_flops(cfg) / (per_call["gemm1"] * 1e-6) / 1e12
         roofline = {"kernel": "moe_gemm1_w4a8 (moe_prefill_kernel<gate|up>, fp16 MFMA)", "bound": "mfma",
@@ -506,7 +508,7 @@ def main():
         torch.cuda.empty_cache()
         pf, _ = measure_layer(torch, W, synth.GROK_PREFILL, min(args.steps, 10), min(args.warmup, 2))
         result["prefill"] = {k: pf[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
-                                                 "layer_mfma_frac", "calls_us", "roofline")}
+                                                 "layer_mfma_frac", "layer_fp8_peak_frac", "calls_us", "roofline")}
         torch.cuda.empty_cache()
     if args.workload == "mixtral_decode" and not args.no_grok_decode:
         # the largest single-GPU decode layer: Grok-1-shaped, 2.42 GB of int4 weights per step
@@ -514,6 +516,19 @@ def main():
         result["grok_decode"] = {k: gd[k] for k in ("value", "unit", "ms_per_step", "steps", "warmup", "config",
                                                      "layer_hbm_frac", "layer_bytes", "calls_us", "roofline")}
         torch.cuda.empty_cache()
+    if args.workload == "mixtral_decode" and not args.no_tp8:
+        # one GPU's 8-way tensor-parallel share of the Grok-1 layer (intermediate 4096 of 32768),
+        # decode and prefill: 302 MB of int4 weights, where a launch's fixed costs weigh most
+        share = {}
+        for c in (synth.GROK_TP8_DECODE, synth.GROK_TP8_PREFILL):
+            decode = W.moe_kernel(c.T) == W.KERNEL_STREAM
+            m, _ = measure_layer(torch, W, c, args.steps if decode else min(args.steps, 10),
+                                 args.warmup if decode else min(args.warmup, 2))
+            share[c.name] = {k: m[k] for k in ("value", "unit", "ms_per_step", "steps", "config", "layer_hbm_frac",
+                                               "layer_mfma_frac", "layer_fp8_peak_frac", "calls_us", "roofline")
+                             if k in m}
+            torch.cuda.empty_cache()
+        result["grok_tp8"] = share
     if args.workload == "mixtral_decode" and not args.no_token_sweep:
         result["token_sweep"] = token_sweep(torch, W, synth.MIXTRAL_DECODE)
         torch.cuda.empty_cache()
