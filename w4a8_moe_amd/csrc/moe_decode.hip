@@ -154,13 +154,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   const int group = bid % p.groups; bid /= p.groups;
   const int slice = bid % p.ksplit;
   const int e = bid / p.ksplit;
-  const int seg0 = p.offsets[e];
-  const int cnt = p.offsets[e + 1] - seg0;
-  if (cnt <= 0) return;                                     // untouched expert: no weight traffic
-  const int nt = min((cnt + 15) >> 4, MAXT);                // column tiles holding rows
   const int k_begin = slice * p.kslice;
   const int k_end = min(p.K, k_begin + p.kslice);
-  const int kc_max = ((p.lds_bytes / (16 * nt)) / (128 * kDepth)) * (128 * kDepth);   // E4M3 rows of 16*nt tokens
 
   // weight row blocks of this wave: gate|up -> (cb, n_out/16 + cb); down -> (2cb, 2cb + 1)
   const int nthr = blockDim.x;                              // p.waves waves
@@ -189,13 +184,19 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   uint32_t mlo = 0x0F0F0F0Fu, mhi = 0xF0F0F0F0u;
   asm volatile("" : "+v"(mlo), "+v"(mhi));
 
-  // prefetch the first kDepth k-steps; the stream runs on across chunk boundaries
+  // prefetch the first kDepth k-steps (before the routing is read: they do not depend on
+  // it); the stream runs on across chunk boundaries
   uint4 q0[kDepth], q1[kDepth];
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) {
     q0[d] = buf_ld16_step(wr, off0, d, ST);
     q1[d] = buf_ld16_step(wr, off1, d, ST1);
   }
+  const int seg0 = p.offsets[e];
+  const int cnt = p.offsets[e + 1] - seg0;
+  if (cnt <= 0) return;                                     // untouched expert: no more weight traffic
+  const int nt = min((cnt + 15) >> 4, MAXT);                // column tiles holding rows
+  const int kc_max = ((p.lds_bytes / (16 * nt)) / (128 * kDepth)) * (128 * kDepth);   // E4M3 rows of 16*nt tokens
   // Staging sources. A thread's staging slots all sit at lane tid % 64 of their 64-slot
   // block, so it always stages column c = tid % 16 of a tile: the activation row behind
   // column c of each tile is looked up once here (a byte offset into act, or out of range
