@@ -1,8 +1,9 @@
 """The one-call layer, moe_layer_w4a8: its output is byte for byte the output of the three
 calls (moe_route_sort_quant, moe_gemm1_w4a8, moe_gemm2_w4a8) on the same inputs, which the
 layer and prefill parity tests hold to the oracle, and it meets the end-to-end bar against
-the oracle itself. The cases cover one to four 16-row column tiles per expert, a split
-down reduction, empty experts, the largest expert count, the tiled kernel above 52 tokens,
+the oracle itself. The cases cover one and two 16-row column tiles per expert, experts with
+more than 32 rows (taken in passes of 32), a split
+down reduction, empty experts, the largest expert count, the tiled kernel above 64 tokens,
 and one workspace reused by calls of different sizes."""
 import numpy as np
 import pytest
@@ -20,22 +21,23 @@ CASES = [
     # I = 37 x 128: a ragged split of the down reduction
     synth.custom_moe("fl_ragged_k", T=32, H=640, I=4736, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=502,
                      x_cfg=502, logit_sigma=1.5),
-    # two experts: every expert holds every token (two and four 16-row column tiles)
+    # two experts: every expert holds every token (two 16-row column tiles; 52 and 64 rows take
+    # two passes of 32)
     synth.custom_moe("fl_two_experts_24", T=24, H=384, I=640, E=2, act=synth.ACT_GELU_TANH, w_cfg=503, x_cfg=503),
     synth.custom_moe("fl_two_experts_52", T=52, H=512, I=1024, E=2, w_cfg=504, x_cfg=504, out_f32=False),
+    synth.custom_moe("fl_two_experts_64", T=64, H=384, I=768, E=2, act=synth.ACT_GELU_ERF, w_cfg=514, x_cfg=514),
     synth.custom_moe("fl_52", T=52, H=512, I=1024, E=8, w_cfg=505, x_cfg=505, logit_sigma=1.5),
-    # the fewest tokens that take the tiled kernel
-    synth.custom_moe("fl_53", T=53, H=512, I=1024, E=8, w_cfg=513, x_cfg=513, logit_sigma=1.5, out_f32=False),
+    synth.custom_moe("fl_64", T=64, H=512, I=1024, E=8, w_cfg=513, x_cfg=513, logit_sigma=1.5, out_f32=False),
     # long down reduction: the down projection split into K-slices
     synth.custom_moe("fl_split_k", T=32, H=256, I=16384, E=8, w_cfg=506, x_cfg=506, out_f32=False),
     synth.custom_moe("fl_empty_experts", T=20, H=256, I=384, E=16, w_cfg=507, x_cfg=507, expert_bias=True,
                      logit_sigma=0.5),
     synth.custom_moe("fl_max_experts", T=24, H=128, I=128, E=256, w_cfg=508, x_cfg=508, out_f32=False,
                      logit_sigma=2.0),
-    # the fewest tokens that take four column tiles (4-wave workgroups), and the most, over 256 experts
+    # the fewest tokens that can need a second pass, and 52 tokens over 256 experts
     synth.custom_moe("fl_33", T=33, H=384, I=768, E=4, act=synth.ACT_GELU_ERF, w_cfg=511, x_cfg=511, out_f32=False),
     synth.custom_moe("fl_max_experts_52", T=52, H=128, I=256, E=256, w_cfg=512, x_cfg=512, logit_sigma=2.0),
-    # above 52 tokens: the routing, the tiled gate|up and down launches in sequence
+    # above 64 tokens: the routing, the tiled gate|up and down launches in sequence
     synth.custom_moe("fl_sequential", T=100, H=256, I=512, E=8, act=synth.ACT_GELU_ERF, w_cfg=509, x_cfg=509,
                      out_f32=False),
 ]

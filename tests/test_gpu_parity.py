@@ -169,6 +169,9 @@ LAYER_CASES = [
     synth.custom_moe("ragged_k", T=32, H=640, I=4736, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=201,
                      x_cfg=201, logit_sigma=1.5),
     synth.custom_moe("chunked", T=52, H=1152, I=1280, E=2, act=synth.ACT_SILU, w_cfg=202, x_cfg=202),
+    # the most tokens the streaming kernel takes: every expert holds 64 rows, two passes of 32
+    synth.custom_moe("two_passes", T=64, H=384, I=640, E=2, act=synth.ACT_GELU_TANH, w_cfg=207, x_cfg=207,
+                     out_f32=False),
     synth.custom_moe("three_tiles", T=40, H=512, I=512, E=3, act=synth.ACT_GELU_TANH, w_cfg=203, x_cfg=203),
     synth.custom_moe("one_token", T=1, H=256, I=256, E=8, w_cfg=204, x_cfg=204),
     synth.custom_moe("many_experts", T=24, H=256, I=384, E=32, w_cfg=205, x_cfg=205, out_f32=False),
@@ -213,13 +216,13 @@ def test_moe_layer_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-# Token counts above 52 take the tiled kernel: tiles of 32, 64 or 256 rows (by the mean rows
+# Token counts above 64 take the tiled kernel: tiles of 32, 64 or 256 rows (by the mean rows
 # per expert) over each expert's segment (ragged last tiles, empty experts), 128-channel gate|up
 # tiles, 256-channel down tiles.
 PREFILL_CASES = [
     synth.custom_moe("pf_small", T=96, H=256, I=512, E=4, w_cfg=301, x_cfg=301),
-    # the fewest tokens that take the tiled kernel (52 take the streaming one)
-    synth.custom_moe("pf_first_tiled", T=53, H=384, I=256, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=307,
+    # the fewest tokens that take the tiled kernel (64 take the streaming one)
+    synth.custom_moe("pf_first_tiled", T=65, H=384, I=256, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=307,
                      x_cfg=307, logit_sigma=1.5),
     synth.custom_moe("pf_ragged", T=300, H=640, I=384, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=302,
                      x_cfg=302, logit_sigma=1.5),

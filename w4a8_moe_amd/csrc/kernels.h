@@ -69,7 +69,7 @@ struct MoeGemmParams {
 #define W4A8_DECODE_LDS_KB 64
 #endif
 constexpr int kDecodeWaves = W4A8_DECODE_WAVES;   // most waves per workgroup of the streaming kernel
-constexpr int kDecodeMaxTiles = 4;                // 16-row column tiles per expert (64 rows)
+constexpr int kDecodeMaxTiles = 2;                // 16-row column tiles per pass (32 rows)
 constexpr int kDecodeLds = W4A8_DECODE_LDS_KB * 1024;
 
 bool decode_fits(int T);             // the streaming kernel handles T tokens

@@ -12,7 +12,9 @@
 // MFMA's sums are not exact; E4M3 values and int4 codes are exact in fp16).
 //
 // Mapping. A workgroup = 8 waves on one expert and one K-slice. The activation rows of
-// the expert (at most 64: four 16-column tiles) for a K-chunk are staged in LDS as their
+// the expert (at most 32 per pass: two 16-column tiles; an expert with more rows takes
+// another pass over its weights, which mostly come from L2 the second time) for a K-chunk
+// are staged in LDS as their
 // E4M3 bytes (16 rows x 4096 K in 64 KB, so up to 16 rows the whole reduction of
 // Mixtral's gate|up is one chunk, with no restaging barrier mid-stream), in the order the
 // MFMA B operand is read (one ds_read_b128 per lane covers two instructions, 1 KB per
@@ -145,7 +147,10 @@ __device__ __forceinline__ void stream_chunk(uint4 (&q0)[kDepth], uint4 (&q1)[kD
     if (d < rem) mma_step<NT>(q0[d], q1[d], lds, s + d, S, nt, lane, mlo, mhi, acc0, acc1);
 }
 
-template <bool GATEUP, int MAXT>
+// MULTI: an expert may hold more rows than MAXT column tiles; the workgroup then takes them
+// in passes of 16 * MAXT rows, streaming its weights once per pass (without MULTI the
+// kernel takes up to 16 * MAXT rows per expert).
+template <bool GATEUP, int MAXT, bool MULTI>
 __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGemmParams p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int tid = threadIdx.x, lane = lane_id();
@@ -193,112 +198,126 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
     q1[d] = buf_ld16_step(wr, off1, d, ST1);
   }
   const int seg0 = p.offsets[e];
-  const int cnt = p.offsets[e + 1] - seg0;
-  if (cnt <= 0) return;                                     // untouched expert: no more weight traffic
-  const int nt = min((cnt + 15) >> 4, MAXT);                // column tiles holding rows
-  const int kc_max = ((p.lds_bytes / (16 * nt)) / (128 * kDepth)) * (128 * kDepth);   // E4M3 rows of 16*nt tokens
-  // Staging sources. A thread's staging slots all sit at lane tid % 64 of their 64-slot
-  // block, so it always stages column c = tid % 16 of a tile: the activation row behind
-  // column c of each tile is looked up once here (a byte offset into act, or out of range
-  // for a column past the expert's rows: the buffer load then returns zeros).
+  const int cnt_all = p.offsets[e + 1] - seg0;
+  if (cnt_all <= 0) return;                                 // untouched expert: no more weight traffic
   const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
       (void*)p.act, (short)0, (int)((GATEUP ? p.P / 2 : p.P) * p.K), 0x00020000);
-  uint32_t srow[MAXT];
+  for (int c0 = 0;; c0 += 16 * MAXT) {
+    const int cnt = MULTI ? min(cnt_all - c0, 16 * MAXT) : cnt_all;   // this pass's rows
+    const int rs0 = seg0 + c0;                                // its first sorted row
+    const int nt = min((cnt + 15) >> 4, MAXT);                // column tiles holding rows
+    const int kc_max = ((p.lds_bytes / (16 * nt)) / (128 * kDepth)) * (128 * kDepth);   // E4M3 rows of 16*nt tokens
+    // Staging sources. A thread's staging slots all sit at lane tid % 64 of their 64-slot
+    // block, so it always stages column c = tid % 16 of a tile: the activation row behind
+    // column c of each tile is looked up once here (a byte offset into act, or out of range
+    // for a column past the expert's rows: the buffer load then returns zeros).
+    uint32_t srow[MAXT];
 #pragma unroll
-  for (int j = 0; j < MAXT; ++j) {
-    const int col = j * 16 + (tid & 15);
-    const int r = GATEUP ? (p.sorted_pair[seg0 + min(col, cnt - 1)] >> 1) : seg0 + min(col, cnt - 1);
-    srow[j] = col < cnt ? (uint32_t)r * (uint32_t)p.K : kOutOfRange;
-  }
-  int sg = 0;                                               // k-steps consumed so far
-  for (int kc0 = k_begin; kc0 < k_end; kc0 += kc_max) {
-    const int klen = min(kc_max, k_end - kc0);
-    const int S = klen >> 7;                                // k-steps in this chunk
-    if (kc0 != k_begin) lds_barrier();                      // LDS reuse
-    // ---- stage the activation rows of this chunk as E4M3 bytes. Unit = 16 codes of one
-    //      row: (tile j, k-step s, half h, lane c + 16 g) -> 16 bytes at
-    //      ((j*S + s)*2 + h)*1024 + lane*16, codes 32 g + 16 h .. +16 of the k-step.
-    {
-      // Buffer loads straight into LDS (no registers, so all of a wave's units are in
-      // flight at once): one instruction moves a 64-unit block (tile j, k-step st, half h)
-      // = v / 64, lane (c + 16 gg) to v * 16. Lanes of a column past the expert's rows
-      // load out of range, which writes zeros.
-      const int blocks = nt * S * 2;
-      for (int blk = wave; blk < blocks; blk += nthr / kWave) {
-        const int h = blk & 1, js = blk >> 1;
-        const int j = js / S, st = js - j * S;
-        uint32_t base = srow[0];
-#pragma unroll
-        for (int jj = 1; jj < MAXT; ++jj) base = j == jj ? srow[jj] : base;
-        const uint32_t kk = (uint32_t)(st * 128 + (lane >> 4) * 32 + h * 16);
-        const uint32_t off = base != kOutOfRange ? base + kc0 + kk : kOutOfRange;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
-                                                 off, 0, 0, 0);
-      }
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);            // this wave's LDS loads (vmcnt, not lgkmcnt)
+    for (int j = 0; j < MAXT; ++j) {
+      const int col = j * 16 + (tid & 15);
+      const int r = GATEUP ? (p.sorted_pair[rs0 + min(col, cnt - 1)] >> 1) : rs0 + min(col, cnt - 1);
+      srow[j] = col < cnt ? (uint32_t)r * (uint32_t)p.K : kOutOfRange;
     }
-    lds_barrier();
-    // ---- stream the weights of this chunk
+    int sg = 0;                                               // k-steps consumed so far
+    for (int kc0 = k_begin; kc0 < k_end; kc0 += kc_max) {
+      const int klen = min(kc_max, k_end - kc0);
+      const int S = klen >> 7;                                // k-steps in this chunk
+      if (kc0 != k_begin) lds_barrier();                      // LDS reuse
+      // ---- stage the activation rows of this chunk as E4M3 bytes. Unit = 16 codes of one
+      //      row: (tile j, k-step s, half h, lane c + 16 g) -> 16 bytes at
+      //      ((j*S + s)*2 + h)*1024 + lane*16, codes 32 g + 16 h .. +16 of the k-step.
+      {
+        // Buffer loads straight into LDS (no registers, so all of a wave's units are in
+        // flight at once): one instruction moves a 64-unit block (tile j, k-step st, half h)
+        // = v / 64, lane (c + 16 gg) to v * 16. Lanes of a column past the expert's rows
+        // load out of range, which writes zeros.
+        const int blocks = nt * S * 2;
+        for (int blk = wave; blk < blocks; blk += nthr / kWave) {
+          const int h = blk & 1, js = blk >> 1;
+          const int j = js / S, st = js - j * S;
+          uint32_t base = srow[0];
+#pragma unroll
+          for (int jj = 1; jj < MAXT; ++jj) base = j == jj ? srow[jj] : base;
+          const uint32_t kk = (uint32_t)(st * 128 + (lane >> 4) * 32 + h * 16);
+          const uint32_t off = base != kOutOfRange ? base + kc0 + kk : kOutOfRange;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, (__attribute__((address_space(3))) void*)(lds + blk * 1024), 16,
+                                                   off, 0, 0, 0);
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);            // this wave's LDS loads (vmcnt, not lgkmcnt)
+      }
+      lds_barrier();
+      // ---- stream the weights of this chunk
+      if (has_work) {
+        stream_chunk<MAXT>(q0, q1, wr, off0, off1, ST, ST1, sg, lds, S, nt, lane, mlo, mhi, acc0, acc1);
+      }
+      sg += S;
+    }
+    if (!MULTI && !has_work) return;
     if (has_work) {
-      stream_chunk<MAXT>(q0, q1, wr, off0, off1, ST, ST1, sg, lds, S, nt, lane, mlo, mhi, acc0, acc1);
+      // ---- epilogue: lane holds rows 4g..4g+3 of each block, column (token row) j*16 + i
+      const float* ws = p.w_scale + (size_t)e * p.Nw;
+      const float k0 = p.s_act;
+#pragma unroll
+      for (int j = 0; j < MAXT; ++j) {
+        const int col = j * 16 + i;
+        if (j >= nt || col >= cnt) continue;
+        const int r = rs0 + col;
+        if (GATEUP) {
+          const int nb = cb * 16 + 4 * g;
+          const float4 sg4 = *reinterpret_cast<const float4*>(ws + nb);
+          const float4 su4 = *reinterpret_cast<const float4*>(ws + p.n_out + nb);
+          float gv[4], uv[4], av[4];
+          const float sgv[4] = {sg4.x, sg4.y, sg4.z, sg4.w}, suv[4] = {su4.x, su4.y, su4.z, su4.w};
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            gv[v] = acc0[j][v] * k0 * sgv[v];
+            uv[v] = acc1[j][v] * k0 * suv[v];
+            av[v] = requant_value_rt(gv[v], uv[v], p.s_a, p.inv_s_a, p.act_fn);
+          }
+          *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
+          if (p.dbg) {
+            float* d = p.dbg + (size_t)r * 2 * p.n_out;
+            *reinterpret_cast<float4*>(d + nb) = make_float4(gv[0], gv[1], gv[2], gv[3]);
+            *reinterpret_cast<float4*>(d + p.n_out + nb) = make_float4(uv[0], uv[1], uv[2], uv[3]);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            if (b == 1 && !has1) break;
+            const int nb = (b == 0 ? blk0 : blk1) * 16 + 4 * g;
+            const v4f acc = b == 0 ? acc0[j] : acc1[j];
+            const float4 sw = *reinterpret_cast<const float4*>(ws + nb);
+            float4 o;
+            o.x = acc[0] * k0 * sw.x;
+            o.y = acc[1] * k0 * sw.y;
+            o.z = acc[2] * k0 * sw.z;
+            o.w = acc[3] * k0 * sw.w;
+            *reinterpret_cast<float4*>(p.partial + ((size_t)slice * p.P + r) * p.n_out + nb) = o;
+          }
+        }
+      }
     }
-    sg += S;
-  }
-  if (!has_work) return;
-
-  // ---- epilogue: lane holds rows 4g..4g+3 of each block, column (token row) j*16 + i
-  const float* ws = p.w_scale + (size_t)e * p.Nw;
-  const float k0 = p.s_act;
+    if (!MULTI || c0 + 16 * MAXT >= cnt_all) break;
+    // the next pass: LDS reuse, the weight stream again from the first k-step, fresh sums
+    lds_barrier();
 #pragma unroll
-  for (int j = 0; j < MAXT; ++j) {
-    const int col = j * 16 + i;
-    if (j >= nt || col >= cnt) continue;
-    const int r = seg0 + col;
-    if (GATEUP) {
-      const int nb = cb * 16 + 4 * g;
-      const float4 sg4 = *reinterpret_cast<const float4*>(ws + nb);
-      const float4 su4 = *reinterpret_cast<const float4*>(ws + p.n_out + nb);
-      float gv[4], uv[4], av[4];
-      const float sgv[4] = {sg4.x, sg4.y, sg4.z, sg4.w}, suv[4] = {su4.x, su4.y, su4.z, su4.w};
+    for (int d = 0; d < kDepth; ++d) {
+      q0[d] = buf_ld16_step(wr, off0, d, ST);
+      q1[d] = buf_ld16_step(wr, off1, d, ST1);
+    }
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        gv[v] = acc0[j][v] * k0 * sgv[v];
-        uv[v] = acc1[j][v] * k0 * suv[v];
-        av[v] = requant_value_rt(gv[v], uv[v], p.s_a, p.inv_s_a, p.act_fn);
-      }
-      *reinterpret_cast<uint32_t*>(p.a_out + (size_t)r * p.n_out + nb) = pack4_e4m3(av[0], av[1], av[2], av[3]);
-      if (p.dbg) {
-        float* d = p.dbg + (size_t)r * 2 * p.n_out;
-        *reinterpret_cast<float4*>(d + nb) = make_float4(gv[0], gv[1], gv[2], gv[3]);
-        *reinterpret_cast<float4*>(d + p.n_out + nb) = make_float4(uv[0], uv[1], uv[2], uv[3]);
-      }
-    } else {
-#pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        if (b == 1 && !has1) break;
-        const int nb = (b == 0 ? blk0 : blk1) * 16 + 4 * g;
-        const v4f acc = b == 0 ? acc0[j] : acc1[j];
-        const float4 sw = *reinterpret_cast<const float4*>(ws + nb);
-        float4 o;
-        o.x = acc[0] * k0 * sw.x;
-        o.y = acc[1] * k0 * sw.y;
-        o.z = acc[2] * k0 * sw.z;
-        o.w = acc[3] * k0 * sw.w;
-        *reinterpret_cast<float4*>(p.partial + ((size_t)slice * p.P + r) * p.n_out + nb) = o;
-      }
+    for (int j = 0; j < MAXT; ++j) {
+      acc0[j] = v4f{0.f, 0.f, 0.f, 0.f}; acc1[j] = acc0[j];
     }
   }
 }
 
-// The streaming kernel takes up to 52 tokens (at most four 16-row column tiles per
-// expert); the tiled kernel is faster from about 56. Measured gate|up / down, us, streaming
-// against tiled: Mixtral-shaped 48 tokens 105.2 / 51.3 against 107.8 / 58.5, 52 tokens
-// 99.0 / 51.1 against 98.8 / 61.6, 56 tokens 109.7 / 61.4 against 96.7 / 62.2, 64 tokens
-// 114.3 / 65.3 against 96.7 / 63.3; Grok-1-shaped 48 tokens 311.3 / 176.2 against 306.8 /
-// 179.0, 64 tokens 347.6 / 193.7 against 291.1 / 181.9 (one GPU's 8-way share of Grok-1
-// keeps preferring streaming up to 56 tokens: 82.9 against 90.1 us for both GEMMs).
-constexpr int kStreamMaxTokens = 52;
-static_assert(kStreamMaxTokens <= 16 * kDecodeMaxTiles, "an expert's rows fit the column tiles");
+// The streaming kernel takes up to 64 tokens, the tiled kernel above. Measured gate|up /
+// down, us, streaming (two column tiles, passes of 32 rows) against tiled: Mixtral-shaped 56
+// tokens 98.4 / 47.9 against 101.0 / 61.7, 64 tokens 102.6 / 53.1 against 103.0 / 63.6; one
+// GPU's 8-way share of Grok-1 at 64 tokens 48.2 / 32.1 against 59.5 / 31.2; Grok-1-shaped
+// 64 tokens 297.1 / 191.9 against 293.5 / 187.1.
+constexpr int kStreamMaxTokens = 64;
 bool decode_fits(int T) { return T <= kStreamMaxTokens; }
 
 // CUs of the current device, looked up once per device. Each slot is an atomic, so calls
@@ -349,14 +368,16 @@ static double plan_down(MoeGemmParams& p, int wmax, long experts, long slots) {
   return best;
 }
 
-// Four column tiles (33 to 52 tokens) take 4-wave workgroups: that kernel needs ~180 registers
-// per lane, so a CU holds 8 of its waves, as two workgroups of 4 rather than one of 8, which
-// keeps the two-per-CU slot count the plans assume. Mixtral-shaped gate|up at 40, 48, 64
-// tokens: 106 -> 98, 114 -> 103, 121 -> 111 us; down at 48 tokens 57 -> 49 us.
+// Above 32 tokens the kernel keeps two column tiles and takes an expert's rows in passes of
+// 32 (a second pass only for an expert with more than 32 rows). Against four column tiles
+// (which needed ~180 registers per lane and so 4-wave workgroups), measured gate|up / down,
+// us: Mixtral-shaped 33 tokens 96.4 / 49.7 -> 86.7 / 42.3, 40 tokens 100.4 / 50.2 -> 87.8 /
+// 42.9, 48 tokens 105.6 / 50.6 -> 91.1 / 49.1; Grok-1-shaped 40 tokens 299.7 / 171.8 -> 272.2
+// / 161.5; one GPU's 8-way share of Grok-1 at 48 tokens 43.7 / 34.1 -> 39.6 / 28.5.
 void plan_decode(MoeGemmParams& p, bool gateup) {
   // an expert never holds more rows than there are tokens (its two slots differ)
   const int T = p.P / 2;
-  p.max_tiles = T <= 16 ? 1 : (T <= 32 ? 2 : 4);
+  p.max_tiles = T <= 16 ? 1 : 2;
   p.lds_bytes = kDecodeLds;
   if (gateup) {
     // The whole reduction (the fused epilogue needs it). Waves per workgroup (16 channels
@@ -372,7 +393,6 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     double best = -1.0;
     for (int w : {8, 7, 4}) {
       if (w > kDecodeWaves) continue;
-      if (p.max_tiles >= 4 && w != 4) continue;             // four column tiles: see above
       const int groups = (p.n_out + 16 * w - 1) / (16 * w);
       const double fill = round_fill((long)groups * experts, slots);
       if (fill > best + 1e-9) {
@@ -387,7 +407,7 @@ void plan_decode(MoeGemmParams& p, bool gateup) {
     // us; a single round keeps 8: Mixtral shape 50.0 us, 58.6 with 6).
     const long experts = std::min(p.E, 2 * T);
     const long slots = 2L * device_cus();
-    const double fill = plan_down(p, p.max_tiles >= 4 ? 4 : kDecodeWaves, experts, slots);
+    const double fill = plan_down(p, kDecodeWaves, experts, slots);
     if ((long)p.groups * p.ksplit * experts > slots && p.waves > 6) {
       MoeGemmParams q = p;
       if (plan_down(q, std::min(6, kDecodeWaves), experts, slots) >= fill - 0.02) {
@@ -401,12 +421,15 @@ template <bool GATEUP>
 static void launch_decode_t(const MoeGemmParams& p, hipStream_t st) {
   const unsigned grid = (unsigned)(p.groups * p.ksplit * p.E);
   const dim3 block(p.waves * kWave);
+  // an expert holds at most T rows (its two slots differ); more than the column tiles
+  // take passes
+  const bool multi = p.P / 2 > 16 * p.max_tiles;
   if (p.max_tiles <= 1)
-    hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 1>), dim3(grid), block, p.lds_bytes, st, p);
-  else if (p.max_tiles == 2)
-    hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 2>), dim3(grid), block, p.lds_bytes, st, p);
+    hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 1, false>), dim3(grid), block, p.lds_bytes, st, p);
+  else if (!multi)
+    hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 2, false>), dim3(grid), block, p.lds_bytes, st, p);
   else
-    hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 4>), dim3(grid), block, p.lds_bytes, st, p);
+    hipLaunchKernelGGL((moe_decode_kernel<GATEUP, 2, true>), dim3(grid), block, p.lds_bytes, st, p);
 }
 
 void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st) {
