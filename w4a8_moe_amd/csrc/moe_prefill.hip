@@ -38,7 +38,7 @@
 // both pipelines, so the two give the same bits.
 //
 // Measured on MI355X (Grok-1-shaped prefill, 256-row tiles, rocprofv3 counters): the matrix
-// cores are busy 56.9% (gate|up) and 63.3% (down) of the cycles, at 2.37 and 2.31 GHz; the
+// cores are busy 57% (gate|up) and 62-63% (down) of the cycles, at 2.36-2.37 and 2.26-2.31 GHz; the
 // step's other work (barrier, operand waits, prologue, epilogue) adds to the MFMA time
 // rather than hiding under it with one wave per SIMD.
 #include <algorithm>
