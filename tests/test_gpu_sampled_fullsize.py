@@ -15,6 +15,7 @@ kernel's own codes. The one-call layer, moe_layer_w4a8, gives the same output by
 the three calls.
 """
 import concurrent.futures as cf
+import dataclasses
 
 import numpy as np
 import pytest
@@ -158,11 +159,21 @@ def _run_sampled(cfg, n_tokens, n_out_ch=512):
     torch().cuda.empty_cache()
 
 
-# grouped by model, so that one packing of the weights serves its decode and prefill workloads
-@pytest.mark.parametrize("name,n_tokens", [("mixtral_decode", 32), ("grok_decode", 32), ("grok_prefill", 48),
-                                           ("grok_tp8_decode", 32), ("grok_tp8_prefill", 48)])
-def test_fullsize_sampled(name, n_tokens):
-    _run_sampled(synth.MOE_CONFIGS[name], n_tokens)
+# Grouped by model, so that one packing of the weights serves its decode and prefill workloads.
+# The second case is the Mixtral-shaped decode at 64 tokens, the most the streaming kernel
+# takes, with unequal expert loads (a per-expert router bias): experts 0 and 3 hold 36 and 38
+# rows, taken in two passes of at most 32.
+SKEWED_64 = dict(T=64, expert_bias=True)
+
+
+@pytest.mark.parametrize("name,change,n_tokens", [("mixtral_decode", None, 32), ("mixtral_decode", SKEWED_64, 64),
+                                                  ("grok_decode", None, 32), ("grok_prefill", None, 48),
+                                                  ("grok_tp8_decode", None, 32), ("grok_tp8_prefill", None, 48)],
+                         ids=["mixtral_decode", "mixtral_decode_64_skewed", "grok_decode", "grok_prefill",
+                              "grok_tp8_decode", "grok_tp8_prefill"])
+def test_fullsize_sampled(name, change, n_tokens):
+    cfg = synth.MOE_CONFIGS[name]
+    _run_sampled(cfg if change is None else dataclasses.replace(cfg, **change), n_tokens)
     if name == "grok_tp8_prefill":
         _PACKED.clear()
 
