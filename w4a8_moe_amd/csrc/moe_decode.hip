@@ -127,11 +127,11 @@ __device__ __forceinline__ void stream_chunk(uint4 (&q0)[kDepth], uint4 (&q1)[kD
                                              uint32_t off0, uint32_t off1, int ST, int ST1, int sg,
                                              const uint8_t* lds, int S, int nt, int lane, uint32_t mlo,
                                              uint32_t mhi, v4f* acc0, v4f* acc1) {
-  constexpr int body = NT <= 2 ? kBody : kDepth;            // keep 4-tile code within registers
+  static_assert(NT <= kDecodeMaxTiles, "more column tiles take passes");
   int s = 0;
-  for (; s + body <= S; s += body) {
+  for (; s + kBody <= S; s += kBody) {
 #pragma unroll
-    for (int t = 0; t < body; ++t)
+    for (int t = 0; t < kBody; ++t)
       stream_step<NT>(q0[t % kDepth], q1[t % kDepth], wr, off0, off1, ST, ST1, sg + s + t, lds, s + t, S, nt, lane,
                       mlo, mhi, acc0, acc1);
   }
