@@ -160,9 +160,9 @@ def _run_sampled(cfg, n_tokens, n_out_ch=512):
 
 
 # Grouped by model, so that one packing of the weights serves its decode and prefill workloads.
-# The second case is the Mixtral-shaped decode at 64 tokens, the most the streaming kernel
-# takes, with unequal expert loads (a per-expert router bias): experts 0 and 3 hold 36 and 38
-# rows, taken in two passes of at most 32.
+# The second case is the Mixtral-shaped decode at 64 tokens with unequal expert loads (a
+# per-expert router bias): experts 0 and 3 hold 36 and 38 rows, which the streaming kernel
+# takes in two passes of at most 32.
 SKEWED_64 = dict(T=64, expert_bias=True)
 
 

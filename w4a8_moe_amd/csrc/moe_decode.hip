@@ -312,12 +312,14 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   }
 }
 
-// The streaming kernel takes up to 64 tokens, the tiled kernel above. Measured gate|up /
-// down, us, streaming (two column tiles, passes of 32 rows) against tiled: Mixtral-shaped 56
-// tokens 98.4 / 47.9 against 101.0 / 61.7, 64 tokens 102.6 / 53.1 against 103.0 / 63.6; one
-// GPU's 8-way share of Grok-1 at 64 tokens 48.2 / 32.1 against 59.5 / 31.2; Grok-1-shaped
-// 64 tokens 297.1 / 191.9 against 293.5 / 187.1.
-constexpr int kStreamMaxTokens = 64;
+// The streaming kernel takes up to 72 tokens, the tiled kernel above. Measured whole layer
+// steps, us, streaming (two column tiles, passes of 32 rows) against tiled, with the router
+// as drawn and with a per-expert bias (the most rows of an expert in brackets): 72 tokens
+// Mixtral-shaped 156.2 against 166.5 (26), 179.9 against 184.1 (41); one GPU's 8-way share
+// of Grok-1 87.5 against 97.8 (25), 87.1 against 97.6 (30); Grok-1-shaped 486.2 against
+// 492.5 (25), 489.8 against 494.4 (30). At 80 and 88 tokens the Grok-1 shape is 1-4% slower
+// streamed and the biased routers tie or lose; at 128 streaming loses by 16-20%.
+constexpr int kStreamMaxTokens = 72;
 bool decode_fits(int T) { return T <= kStreamMaxTokens; }
 
 // CUs of the current device, looked up once per device. Each slot is an atomic, so calls
