@@ -13,8 +13,7 @@
 //
 // Mapping. A workgroup = 8 waves on one expert and one K-slice. The activation rows of
 // the expert (at most 32 per pass: two 16-column tiles; an expert with more rows takes
-// another pass over its weights, which mostly come from L2 the second time) for a K-chunk
-// are staged in LDS as their
+// another pass over its weights, read again) for a K-chunk are staged in LDS as their
 // E4M3 bytes (16 rows x 4096 K in 64 KB, so up to 16 rows the whole reduction of
 // Mixtral's gate|up is one chunk, with no restaging barrier mid-stream), in the order the
 // MFMA B operand is read (one ds_read_b128 per lane covers two instructions, 1 KB per
