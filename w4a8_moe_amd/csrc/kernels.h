@@ -78,7 +78,7 @@ void plan_decode(MoeGemmParams& p, bool gateup);
 void launch_moe_decode(const MoeGemmParams& p, bool gateup, hipStream_t st);
 
 bool prefill_available();
-int prefill_token_blocks(int P, int E);   // 16-row token blocks per tile of the tiled kernel
+int prefill_token_blocks(int P, int E, bool gateup);   // 16-row token blocks per tile of the tiled kernel
 void plan_prefill(MoeGemmParams& p, bool gateup);   // split-K of the tiled down projection
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st);
 

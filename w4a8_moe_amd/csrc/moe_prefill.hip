@@ -393,7 +393,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_prefill_kernel(MoeGemmParams p
 bool prefill_available() { return true; }
 
 // Token blocks per tile, by the mean rows per expert (P / E): 32-row tiles up to 48 rows,
-// 64-row tiles up to 1536, 256-row tiles above. The 32- and 64-row tiles run two
+// 64-row tiles up to 1536 (gate|up: up to 511), 256-row tiles above. The 32- and 64-row tiles run two
 // workgroups per CU with register rings, and up to about a thousand rows per expert that
 // outweighs reading each weight tile once per 64 rows instead of once per 256; the 256-row
 // tiles win once an expert holds many of them (their weights then come from the caches).
@@ -410,13 +410,19 @@ bool prefill_available() { return true; }
 //                   4096 tokens: 64-row 5949 / 2934, 256-row 6066 / 2921
 //                   8192 tokens: 64-row 11435 / 5652, 256-row 11117 / 5179
 //                  32768 tokens: 64-row 44428 / 21947, 256-row 39594 / 19223
-int prefill_token_blocks(int P, int E) {
+// With 8 waves per 256-row gate|up workgroup those tiles take gate|up from 512 rows per
+// expert on (gate|up, us, 64-row against 256-row tiles, same box): Mixtral-shaped 2048
+// tokens 892 / 855, 4096 tokens 1636 / 1542, 6144 tokens 2529 / 2268; Grok-1-shaped 2048
+// tokens 2933 / 2880, 4096 tokens 5787 / 6032; one GPU's 8-way share of Grok-1 4096 tokens
+// 718 / 700, 6144 tokens 1109 / 1084. The down projection keeps 64-row tiles up to 1536
+// (Mixtral-shaped 2048 tokens 464 against 635 us with 256-row tiles).
+int prefill_token_blocks(int P, int E, bool gateup) {
 #ifdef W4A8_PREFILL_TB
-  (void)P; (void)E;
+  (void)P; (void)E; (void)gateup;
   return W4A8_PREFILL_TB;   // 2, 4 or 16
 #endif
   const int mean = (P + E - 1) / E;
-  return mean <= 48 ? 2 : (mean <= 1536 ? 4 : 16);
+  return mean <= 48 ? 2 : (mean <= (gateup ? 511 : 1536) ? 4 : 16);
 }
 
 // Split of the down projection's reduction. Gate|up needs the whole K (its epilogue forms
@@ -430,7 +436,7 @@ void plan_prefill(MoeGemmParams& p, bool gateup) {
   p.ksplit = 1;
   p.kslice = p.K;
   if (gateup) return;
-  const int pm = 16 * prefill_token_blocks(p.P, p.E);
+  const int pm = 16 * prefill_token_blocks(p.P, p.E, false);
   const int est_mtiles = std::max((p.P + pm - 1) / pm, std::min(p.E, p.P));   // M-tiles holding rows
   const long tiles = (long)est_mtiles * ((p.Nw + kPN - 1) / kPN);
   const long want = 2L * device_cus();
@@ -509,7 +515,7 @@ static void launch_tb(const MoeGemmParams& p, bool gateup, hipStream_t st) {
 }
 
 void launch_moe_prefill(const MoeGemmParams& p, bool gateup, hipStream_t st) {
-  const int tb = prefill_token_blocks(p.P, p.E);
+  const int tb = prefill_token_blocks(p.P, p.E, gateup);
   if (tb == 2) launch_tb<2>(p, gateup, st);
   else if (tb == 4) launch_tb<4>(p, gateup, st);
   else launch_tb<16>(p, gateup, st);
