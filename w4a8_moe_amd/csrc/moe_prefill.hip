@@ -17,19 +17,21 @@
 // rows (BPW = 16 / NW blocks of 16) against all TB token blocks, so its int4 codes go from
 // global memory straight into its own registers, are widened there and used as MFMA
 // operands without an LDS round trip. For gate|up the rows are gate channels and the
-// matching up channels (half each), so act(gate) * up is formed in registers. Only the token tile (TB*16 rows x 128 K per k-step, gathered through
-// sorted_pair for gate|up) is shared through LDS, double buffered: each thread widens its
+// matching up channels (half each), so act(gate) * up is formed in registers. Only the
+// token tile (TB*16 rows x 128 K per k-step, gathered through sorted_pair for gate|up) is
+// shared through LDS, double buffered: each thread widens its
 // staging chunks to fp16 once, and the waves read finished MFMA operands (1 KB per token
 // block and K-part, lane l's 16 bytes at 16 l: no bank conflicts on either side).
 //
 // Pipeline of the 256-row tiles, per k-step s (one barrier each): issue the weight loads of
 // step s+2; then walk the token blocks, the next block's operands read ahead, widening the
-// step's 4 BPW weight words (BPW blocks x 4 MFMAs of K = 32) K-part by K-part inside the first
-// token block, storing the tokens of step s+1 (loaded one step earlier) into the other LDS
-// buffer and issuing the token loads of step s+2 on the way. Loads past the last k-step read in-bounds data or zeros and
-// are never used, so the loop has no branches. (The compiler moves a step's fresh weight
-// loads into the ring by copies at the end of the step, which waits for them: in effect the
-// weights run one step ahead, which the long steps of these tiles cover.)
+// step's 4 BPW weight words (BPW blocks x 4 MFMAs of K = 32) K-part by K-part inside the
+// first token block, storing the tokens of step s+1 (loaded one step earlier) into the other
+// LDS buffer and issuing the token loads of step s+2 on the way. Loads past the last k-step
+// read in-bounds data or zeros and are never used, so the loop has no branches. (The
+// compiler moves a step's fresh weight loads into the ring by copies at the end of the step,
+// which waits for them: in effect the weights run one step ahead, which the long steps of
+// these tiles cover.)
 //
 // The 32- and 64-row tiles have short steps (32 or 64 MFMAs per wave), so they keep their
 // loads R steps ahead in register rings without copies (the loop body unrolled by R, each
