@@ -94,7 +94,8 @@ def _check_route(logits):
 
 @pytest.mark.parametrize("T,E,sigma", [(16, 4, 1.0), (32, 8, 1.5), (1, 2, 1.0), (255, 8, 1.5), (256, 8, 1.5),
                                        (257, 8, 1.5), (5000, 8, 1.5), (1000, 64, 1.0), (300, 256, 1.0),
-                                       (4097, 3, 2.0)])
+                                       (4097, 3, 2.0), (20000, 8, 1.5), (33000, 256, 1.0), (40000, 3, 2.0),
+                                       (70000, 100, 1.0)])
 def test_route_sort_bit_exact(T, E, sigma):
     rng = np.random.default_rng(T * 7 + E)
     _check_route((rng.standard_normal((T, E)) * sigma).astype(np.float32))

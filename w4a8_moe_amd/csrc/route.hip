@@ -146,29 +146,56 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 }
 
 // Phase 2 (one block): counts, offsets, and each block's base position per expert.
+// Thread (s, e) owns expert e over a segment of consecutive blocks (256 / E segments),
+// so the serial walk per thread is nb / (256 / E) blocks and each step's loads, over
+// consecutive e, are contiguous. Integer sums: the result does not depend on the split.
 __global__ __launch_bounds__(kRouteThreads) void route_scan_kernel(
     int nb, int E, const int32_t* __restrict__ cnt, int32_t* __restrict__ base,
     int32_t* __restrict__ counts, int32_t* __restrict__ offsets) {
-  extern __shared__ int tot[];                 // [E]
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+  extern __shared__ int sm[];
+  int* part = sm;                              // [S][E]: segment sums, then exclusive scans
+  int* tot = sm + kRouteThreads;               // [E]
+  int* off = tot + E;                          // [E]
+  const int S = kRouteThreads / E;             // E <= 256, so S >= 1
+  const int L = (nb + S - 1) / S;              // blocks per segment
+  const int t = threadIdx.x, s = t / E, e = t - s * E;
+  const bool act = s < S;
+  const int b0 = s * L, b1 = min(nb, b0 + L);
+  if (act) {
+    int sum = 0;
+    for (int b = b0; b < b1; ++b) sum += cnt[(size_t)b * E + e];
+    part[t] = sum;
+  }
+  __syncthreads();
+  if (t < E) {
     int run = 0;
-    for (int b = 0; b < nb; ++b) {
+    for (int q = 0; q < S; ++q) { const int v = part[q * E + t]; part[q * E + t] = run; run += v; }
+    tot[t] = run;
+    counts[t] = run;
+  }
+  __syncthreads();
+  if (t < kWave) {
+    // wave 0: exclusive scan of the totals over the experts, 64 at a time
+    int carry = 0;
+    for (int c0 = 0; c0 < E; c0 += kWave) {
+      const int v = c0 + t < E ? tot[c0 + t] : 0;
+      int incl = v;
+      for (int d = 1; d < kWave; d <<= 1) {
+        const int u = __shfl_up(incl, d);
+        if (t >= d) incl += u;
+      }
+      if (c0 + t < E) { off[c0 + t] = carry + incl - v; offsets[c0 + t] = carry + incl - v; }
+      carry += __shfl(incl, kWave - 1);
+    }
+    if (t == 0) offsets[E] = carry;
+  }
+  __syncthreads();
+  if (act) {
+    int run = off[e] + part[t];
+    for (int b = b0; b < b1; ++b) {
       base[(size_t)b * E + e] = run;
       run += cnt[(size_t)b * E + e];
     }
-    tot[e] = run;
-    counts[e] = run;
-  }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int e = 0; e < E; ++e) { int c = tot[e]; tot[e] = run; offsets[e] = run; run += c; }
-    offsets[E] = run;
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    const int o = tot[e];
-    for (int b = 0; b < nb; ++b) base[(size_t)b * E + e] += o;
   }
 }
 
@@ -216,8 +243,8 @@ void launch_route_sort(const float* logits, int T, int E, int32_t* ids, float* t
   int32_t* base = cnt + (size_t)nb * E;
   hipLaunchKernelGGL(route_topk_kernel, dim3(nb), dim3(kRouteThreads), E * sizeof(int), st, logits, T, E,
                      ids, tw, cnt);
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), E * sizeof(int), st, nb, E, cnt, base,
-                     counts, offsets);
+  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(kRouteThreads), (kRouteThreads + 2 * E) * sizeof(int), st,
+                     nb, E, cnt, base, counts, offsets);
   hipLaunchKernelGGL(route_scatter_kernel, dim3(nb), dim3(kRouteThreads), kRouteWaves * E * sizeof(int), st,
                      T, E, ids, base, sorted_pair, pair_pos);
 }
