@@ -101,6 +101,14 @@ def test_route_sort_bit_exact(T, E, sigma):
     _check_route((rng.standard_normal((T, E)) * sigma).astype(np.float32))
 
 
+@pytest.mark.parametrize("T,E", [(1 << 22, 8), ((1 << 17) + 5, 256)], ids=["max_tokens", "max_experts"])
+def test_route_sort_largest(T, E):
+    """The largest token count the calls accept (2^22: 16384 blocks of 256 tokens in the scan,
+    512 per segment) and the largest expert count (one segment of 513 blocks per expert)."""
+    rng = np.random.default_rng(E)
+    _check_route((rng.standard_normal((T, E)) * 1.5).astype(np.float32))
+
+
 @pytest.mark.parametrize("T,E,H", [(32, 8, 4096), (1, 2, 136), (256, 8, 520), (257, 8, 264), (3, 16, 9), (0, 8, 64)])
 def test_route_sort_quant_matches_separate_calls(T, E, H):
     """One launch (T <= 256) or the multi-kernel routing then the quantization: the same
