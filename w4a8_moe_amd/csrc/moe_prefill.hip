@@ -399,7 +399,7 @@ bool prefill_available() { return true; }
 // workgroups per CU with register rings, and up to about a thousand rows per expert that
 // outweighs reading each weight tile once per 64 rows instead of once per 256; the 256-row
 // tiles win once an expert holds many of them (their weights then come from the caches).
-// 128-row tiles were never the fastest. Measured gate|up / down, us (same box):
+// 128-row tiles were never the fastest. Measured gate|up / down, us (same GPU):
 //   Mixtral-shaped   96 tokens: 32-row 143 / 79,   64-row 140 / 81
 //                   192 tokens: 32-row 168 / 98,   64-row 189 / 104
 //                   256 tokens: 32-row 208 / 110,  64-row 199 / 114
@@ -413,7 +413,7 @@ bool prefill_available() { return true; }
 //                   8192 tokens: 64-row 11435 / 5652, 256-row 11117 / 5179
 //                  32768 tokens: 64-row 44428 / 21947, 256-row 39594 / 19223
 // With 8 waves per 256-row gate|up workgroup those tiles take gate|up from 512 rows per
-// expert on (gate|up, us, 64-row against 256-row tiles, same box): Mixtral-shaped 2048
+// expert on (gate|up, us, 64-row against 256-row tiles, same GPU): Mixtral-shaped 2048
 // tokens 892 / 855, 4096 tokens 1636 / 1542, 6144 tokens 2529 / 2268; Grok-1-shaped 2048
 // tokens 2933 / 2880, 4096 tokens 5787 / 6032; one GPU's 8-way share of Grok-1 4096 tokens
 // 718 / 700, 6144 tokens 1109 / 1084. The down projection keeps 64-row tiles up to 1536
