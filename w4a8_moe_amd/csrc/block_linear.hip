@@ -36,6 +36,16 @@
 
 namespace w4a8 {
 
+#ifndef W4A8_GEMV_NT
+#define W4A8_GEMV_NT 0
+#endif
+// 16 bytes of weights (nontemporal hint behind the knob)
+__device__ __forceinline__ uint4 ld_w16(const uint8_t* p) {
+  typedef unsigned u4v __attribute__((ext_vector_type(4)));
+  if (W4A8_GEMV_NT) return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u4v*>(p)));
+  return *reinterpret_cast<const uint4*>(p);
+}
+
 #ifndef W4A8_BL_SPLIT
 #define W4A8_BL_SPLIT 4
 #endif
@@ -82,8 +92,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
 #pragma unroll
   for (int d = 0; d < kBlDepth; ++d)
     if (kb_begin + d < kb_end) {
-      q0[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128);
-      q1[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128 + 16);
+      q0[d] = ld_w16(wp + (kb_begin + d) * 128);
+      q1[d] = ld_w16(wp + (kb_begin + d) * 128 + 16);
     }
   // ---- stage x: unit (kb, j, g, m) = 8 bf16 = x[m][kb*128 + g*32 + j*8 .. +8], stored at
   //      ((kb*4 + j)*4 + g)*M + m, so lane (m, g) of MFMA j reads 16 contiguous bytes.
@@ -105,8 +115,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_kernel
       if (kb < kb_end) {
         const uint4 a0 = q0[d], a1 = q1[d];
         if (kb + kBlDepth < kb_end) {
-          q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128);
-          q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128 + 16);
+          q0[d] = ld_w16(wp + (kb + kBlDepth) * 128);
+          q1[d] = ld_w16(wp + (kb + kBlDepth) * 128 + 16);
         }
         const uint32_t c[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         v4f blk = {0.f, 0.f, 0.f, 0.f};
@@ -180,8 +190,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_wide_k
   for (int t = 0; t < NT; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
   uint4 q0 = make_uint4(0u, 0u, 0u, 0u), q1 = q0;
   if (kb_begin < kb_end) {
-    q0 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128);
-    q1 = *reinterpret_cast<const uint4*>(wp + kb_begin * 128 + 16);
+    q0 = ld_w16(wp + kb_begin * 128);
+    q1 = ld_w16(wp + kb_begin * 128 + 16);
   }
   const int units = kBlSplit * CK * 16 * M;
   for (int c = 0; c < chunks; ++c) {
@@ -203,8 +213,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_block_linear_wide_k
       if (kb < kb_end) {
         const uint4 a0 = q0, a1 = q1;
         if (kb + 1 < kb_end) {
-          q0 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128);
-          q1 = *reinterpret_cast<const uint4*>(wp + (kb + 1) * 128 + 16);
+          q0 = ld_w16(wp + (kb + 1) * 128);
+          q1 = ld_w16(wp + (kb + 1) * 128 + 16);
         }
         const uint32_t cw[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
         v4f blk[NT];
@@ -343,8 +353,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
 #pragma unroll
   for (int d = 0; d < kBlDepth; ++d)
     if (kb_begin + d < kb_end) {
-      q0[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128);
-      q1[d] = *reinterpret_cast<const uint4*>(wp + (kb_begin + d) * 128 + 16);
+      q0[d] = ld_w16(wp + (kb_begin + d) * 128);
+      q1[d] = ld_w16(wp + (kb_begin + d) * 128 + 16);
     }
   for (int kb0 = kb_begin; kb0 < kb_end; kb0 += kBlDepth) {
 #pragma unroll
@@ -353,8 +363,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_kernel(
       if (kb < kb_end) {
         const uint4 a0 = q0[d], a1 = q1[d];
         if (kb + kBlDepth < kb_end) {
-          q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128);
-          q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + kBlDepth) * 128 + 16);
+          q0[d] = ld_w16(wp + (kb + kBlDepth) * 128);
+          q1[d] = ld_w16(wp + (kb + kBlDepth) * 128 + 16);
         }
         const uint32_t c[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
@@ -429,8 +439,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
   for (int d = 0; d < D; ++d) {
     const int kb = kb_begin + d;
     if (kb < kb_end) {
-      q0[d] = *reinterpret_cast<const uint4*>(wp + kb * 128);
-      q1[d] = *reinterpret_cast<const uint4*>(wp + kb * 128 + 16);
+      q0[d] = ld_w16(wp + kb * 128);
+      q1[d] = ld_w16(wp + kb * 128 + 16);
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         b0[d][t] = *reinterpret_cast<const uint4*>(xp[t] + kb * 128);
@@ -448,8 +458,8 @@ __global__ __launch_bounds__(RB * kBlSplit * kWave) void fp8_linear_wide_kernel(
 #pragma unroll
         for (int t = 0; t < NT; ++t) { c0[t] = b0[d][t]; c1[t] = b1[d][t]; }
         if (kb + D < kb_end) {
-          q0[d] = *reinterpret_cast<const uint4*>(wp + (kb + D) * 128);
-          q1[d] = *reinterpret_cast<const uint4*>(wp + (kb + D) * 128 + 16);
+          q0[d] = ld_w16(wp + (kb + D) * 128);
+          q1[d] = ld_w16(wp + (kb + D) * 128 + 16);
 #pragma unroll
           for (int t = 0; t < NT; ++t) {
             b0[d][t] = *reinterpret_cast<const uint4*>(xp[t] + (kb + D) * 128);

@@ -33,13 +33,16 @@ namespace w4a8 {
 
 // Tuning knobs (defaults chosen by measurement on MI355X):
 //   W4A8_DECODE_DEPTH     k-steps of weights in flight per wave (LDS chunks hold multiples)
-//   W4A8_DECODE_NT_LOADS  stream the weights with the nontemporal hint (measured slower)
+//   W4A8_DECODE_NT_LOADS  stream the weights with the nontemporal hint (on by default: they are
+//                         read once; whole graph-captured layer steps, us, without / with it:
+//                         Mixtral-shaped 32 tokens 142.5 / 126.6, 16 tokens 140.1 / 123.4, 48 tokens
+//                         151.5 / 136.0; Grok-1-shaped 438.5 / 397.8; one GPU's 8-way share 73.9 / 69.4)
 //   W4A8_DECODE_BODY      k-steps per unrolled loop body
 #ifndef W4A8_DECODE_DEPTH
 #define W4A8_DECODE_DEPTH 4
 #endif
 #ifndef W4A8_DECODE_NT_LOADS
-#define W4A8_DECODE_NT_LOADS 0
+#define W4A8_DECODE_NT_LOADS 1
 #endif
 #ifndef W4A8_DECODE_BODY
 #define W4A8_DECODE_BODY 16

@@ -55,9 +55,14 @@ constexpr int kPN = 256;          // weight rows per tile
 constexpr uint32_t kPOutOfRange = 0x80000000u;   // past every buffer (all are < 2^31 bytes)
 
 // per-lane offset plus a wave-uniform one (the step), added by the load itself
+template <int AUX = 0>
 __device__ __forceinline__ uint4 pf_ld16s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), 0));
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, __builtin_amdgcn_readfirstlane(soff), AUX));
 }
+#ifndef W4A8_PREFILL_NT
+#define W4A8_PREFILL_NT 0
+#endif
+constexpr int kPfWeightAux = W4A8_PREFILL_NT ? 2 : 0;   // cache-policy bits of the weight loads
 
 __device__ __forceinline__ uint32_t word4(const uint4& q, int m) {
   return m == 0 ? q.x : (m == 1 ? q.y : (m == 2 ? q.z : q.w));
@@ -193,8 +198,8 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_prefill_kernel(MoeGemmParams p
     uint4 wc[BPW], wn[BPW];      // raw weights of steps s and s+1
 #pragma unroll
     for (int a = 0; a < BPW; ++a) {
-      wc[a] = pf_ld16s(wr, woff[a], kb * kTileBytes);
-      wn[a] = pf_ld16s(wr, woff[a], (kb + 1) * kTileBytes);
+      wc[a] = pf_ld16s<kPfWeightAux>(wr, woff[a], kb * kTileBytes);
+      wn[a] = pf_ld16s<kPfWeightAux>(wr, woff[a], (kb + 1) * kTileBytes);
     }
     load_tokens(0);
 #pragma unroll
@@ -216,7 +221,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_prefill_kernel(MoeGemmParams p
       for (int a = 0; a < BPW; ++a) {
         wraw[a] = wc[a];
         wc[a] = wn[a];
-        wn[a] = pf_ld16s(wr, woff[a], (uint32_t)((kb + s + 2) * kTileBytes));
+        wn[a] = pf_ld16s<kPfWeightAux>(wr, woff[a], (uint32_t)((kb + s + 2) * kTileBytes));
       }
       // token blocks in order, each block's 16 MFMAs (4 K-parts x 4 weight blocks) together:
       // an accumulator's four MFMAs of the step are adjacent, which keeps every accumulator in
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_prefill_kernel(MoeGemmParams p
     for (int d = 0; d < R; ++d) {
 #pragma unroll
       for (int a = 0; a < BPW; ++a) {
-        wq[d][a] = pf_ld16s(wr, woff[a], (kb + d) * kTileBytes);
+        wq[d][a] = pf_ld16s<kPfWeightAux>(wr, woff[a], (kb + d) * kTileBytes);
         __builtin_amdgcn_sched_barrier(0);                // keep the issue order
       }
 #pragma unroll
@@ -321,7 +326,7 @@ __global__ __launch_bounds__(64 * NW, 1) void moe_prefill_kernel(MoeGemmParams p
         // refill: weights of step s + R into this step's slot; tokens of step s + 1 to LDS,
         // then step s + 1 + R into their slot
 #pragma unroll
-        for (int a = 0; a < BPW; ++a) wq[u][a] = pf_ld16s(wr, woff[a], (uint32_t)((kb + s + R) * kTileBytes));
+        for (int a = 0; a < BPW; ++a) wq[u][a] = pf_ld16s<kPfWeightAux>(wr, woff[a], (uint32_t)((kb + s + R) * kTileBytes));
 #pragma unroll
         for (int j = 0; j < kTJ; ++j) {
           store_tokens(Tn, j, tq[un][j]);
