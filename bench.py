@@ -65,7 +65,10 @@ def bf16_dev(torch, bits, dev):
     return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
 
 
-STEPS_PER_GRAPH = 4      # consecutive layer steps captured in one HIP graph
+# consecutive layer steps captured in one HIP graph: the 32 MoE layers of one Mixtral-8x7B
+# decode forward (Grok-1 has 64). Each graph replay costs about 70 us on the GPU timeline
+# (measured: 4-step graphs 147 us per Mixtral-shaped step, 50-step graphs 128.5 us).
+STEPS_PER_GRAPH = 32
 
 COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_decode": "moe_decode_grok_T32.json",
                  "grok_prefill": "moe_prefill_grok_T32768.json"}
@@ -397,9 +400,13 @@ def measure_layer(torch, W, cfg, steps, warmup):
     ref_out = out1.clone()
     counts = ro["counts"].cpu().numpy()
     ids = ro["ids"].cpu().numpy()
-    graphs1, graphsN = [], []
+    graphs1, graphsN, graphsR = [], [], []
+    rest = steps % STEPS_PER_GRAPH
     for c in range(copies):
-        for n, dst in ((1, graphs1), (STEPS_PER_GRAPH, graphsN)):
+        full = STEPS_PER_GRAPH if steps >= STEPS_PER_GRAPH else 0
+        for n, dst in ((1, graphs1), (full, graphsN), (rest, graphsR)):
+            if n == 0:
+                continue
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
                 for k in range(n):
@@ -408,24 +415,24 @@ def measure_layer(torch, W, cfg, steps, warmup):
     for i in range(warmup):
         graphs1[i % copies].replay()
     torch.cuda.synchronize()
-    for g in (graphs1[0], graphsN[0]):
+    for g in graphs1[:1] + graphsN[:1] + graphsR[:1]:
         out1.zero_()
         g.replay()
         torch.cuda.synchronize()
         if not torch.equal(out1, ref_out):
             raise RuntimeError("graph replay differs from the eager step")
 
-    # ---- timed region: exactly K steps (graphs of STEPS_PER_GRAPH steps, single-step
-    #      graphs for the remainder), wall clock between two synchronizations
+    # ---- timed region: exactly K steps (graphs of STEPS_PER_GRAPH steps, then one graph of
+    #      the remaining K mod STEPS_PER_GRAPH steps), wall clock between two synchronizations
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     done = 0
     while done + STEPS_PER_GRAPH <= steps:
         graphsN[done % copies].replay()
         done += STEPS_PER_GRAPH
-    while done < steps:
-        graphs1[done % copies].replay()
-        done += 1
+    if done < steps:
+        graphsR[done % copies].replay()
+        done += rest
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / steps
@@ -481,7 +488,7 @@ def measure_layer(torch, W, cfg, steps, warmup):
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "intermediate": I, "experts": E, "top_k": 2,
                    "activation": ACT_NAMES[cfg.act], "out": "fp32" if cfg.out_f32 else "bf16",
                    "weight_copies_rotated": copies, "experts_touched": touched,
-                   "steps_per_graph": STEPS_PER_GRAPH},
+                   "steps_per_graph": min(STEPS_PER_GRAPH, steps)},
         **layer_frac,
         "layer_bytes": int(layer_bytes),
         "calls_us": {k: round(v, 2) for k, v in per_call.items()},
