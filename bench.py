@@ -37,7 +37,11 @@ ACT_NAMES = {synth.ACT_SILU: "silu", synth.ACT_GELU_ERF: "gelu_erf", synth.ACT_G
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    # layer steps timed (prefill: at most 10). A timed run carries about 0.7 ms of fixed wall-clock
+    # cost (the first graph launch, the closing synchronization): measured on one GPU, ms per
+    # Mixtral-shaped step, 64 steps 0.138-0.144, 320 steps 0.131, 1024 steps 0.127, against
+    # 0.125 per call timed with events inside one graph; Grok-1-shaped 0.410 / 0.410 / 0.407.
+    ap.add_argument("--steps", type=int, default=1024)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_decode", choices=sorted(synth.MOE_CONFIGS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -66,8 +70,9 @@ def bf16_dev(torch, bits, dev):
 
 
 # consecutive layer steps captured in one HIP graph: the 32 MoE layers of one Mixtral-8x7B
-# decode forward (Grok-1 has 64). Each graph replay costs about 70 us on the GPU timeline
-# (measured: 4-step graphs 147 us per Mixtral-shaped step, 50-step graphs 128.5 us).
+# decode forward (Grok-1 has 64). Measured on one GPU, 64 steps timed, ms per Mixtral- /
+# Grok-1-shaped step: 32 steps per graph 0.142-0.147 / 0.410, 4 steps 0.149-0.153 / 0.422,
+# 1 step 0.155 / 0.431.
 STEPS_PER_GRAPH = 32
 
 COUNTER_FILES = {"mixtral_decode": "moe_decode_mixtral_T32.json", "grok_decode": "moe_decode_grok_T32.json",
@@ -440,7 +445,7 @@ def measure_layer(torch, W, cfg, steps, warmup):
     # ---- per-call duration: one call's launches back to back in a graph, between two HIP
     #      events on the stream the library launches on
 
-    def per_launch_us(fn, n=max(20, steps)):
+    def per_launch_us(fn, n=min(256, max(20, steps))):
         # n calls captured back to back in one graph (so a short call is timed on the GPU, not
         # behind the Python binding's launch cost), replayed between two events on the stream
         return graph_call_us(torch, fn, n)
