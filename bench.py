@@ -254,12 +254,12 @@ def bench_kv_store(torch, W, dev, T=32, D=1024, slots_total=65536, iters=100):
     return {"us": round(us, 3), "tokens": T, "row_elements": D, "timed": f"{iters} calls in one HIP graph"}
 
 
-SWEEP_TOKENS = (32, 48, 72, 73, 128, 256, 512, 1024)
+SWEEP_TOKENS = (32, 48, 80, 81, 128, 256, 512, 1024)
 
 
 def token_sweep(torch, W, base, iters=20):
     """The two grouped GEMMs of the Mixtral-shaped layer at batch sizes around the switch
-    from the streaming kernel (up to 72 tokens) to the tiled one: per T, each call's
+    from the streaming kernel (up to 80 tokens) to the tiled one: per T, each call's
     average time over back-to-back launches, its HBM rate (touched experts' weights and
     scales, activations in and out) and its matrix rate (routed rows only). The weights
     are rotated over two copies so that they stream from HBM."""

@@ -27,9 +27,9 @@ def test_exports_every_declared_function(L):
 
 
 def test_kernel_choice(L):
-    # up to 72 tokens the streaming kernel, above it the tiled one
-    assert [W.moe_kernel(t) for t in (0, 1, 32, 33, 64, 72)] == [W.KERNEL_STREAM] * 6
-    assert [W.moe_kernel(t) for t in (73, 1024, 32768)] == [W.KERNEL_TILED] * 3
+    # up to 80 tokens the streaming kernel, above it the tiled one
+    assert [W.moe_kernel(t) for t in (0, 1, 32, 33, 64, 72, 80)] == [W.KERNEL_STREAM] * 7
+    assert [W.moe_kernel(t) for t in (81, 1024, 32768)] == [W.KERNEL_TILED] * 3
 
 
 def test_status_strings(L):

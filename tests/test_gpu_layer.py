@@ -3,7 +3,7 @@ calls (moe_route_sort_quant, moe_gemm1_w4a8, moe_gemm2_w4a8) on the same inputs,
 layer and prefill parity tests hold to the oracle, and it meets the end-to-end bar against
 the oracle itself. The cases cover one and two 16-row column tiles per expert, experts with
 more than 32 rows (taken in passes of 32, up to three), a split
-down reduction, empty experts, the largest expert count, the tiled kernel above 72 tokens,
+down reduction, empty experts, the largest expert count, the tiled kernel above 80 tokens,
 and one workspace reused by calls of different sizes."""
 import numpy as np
 import pytest
@@ -28,9 +28,11 @@ CASES = [
     synth.custom_moe("fl_two_experts_64", T=64, H=384, I=768, E=2, act=synth.ACT_GELU_ERF, w_cfg=514, x_cfg=514),
     synth.custom_moe("fl_52", T=52, H=512, I=1024, E=8, w_cfg=505, x_cfg=505, logit_sigma=1.5),
     synth.custom_moe("fl_64", T=64, H=512, I=1024, E=8, w_cfg=513, x_cfg=513, logit_sigma=1.5, out_f32=False),
-    # the most tokens the streaming kernel takes, two experts of 72 rows: three passes
+    # two experts of 72 rows, and the most tokens the streaming kernel takes (80 rows each):
+    # three passes
     synth.custom_moe("fl_two_experts_72", T=72, H=256, I=640, E=2, act=synth.ACT_SILU, w_cfg=515, x_cfg=515,
                      out_f32=False),
+    synth.custom_moe("fl_two_experts_80", T=80, H=384, I=512, E=2, act=synth.ACT_GELU_ERF, w_cfg=516, x_cfg=516),
     # long down reduction: the down projection split into K-slices
     synth.custom_moe("fl_split_k", T=32, H=256, I=16384, E=8, w_cfg=506, x_cfg=506, out_f32=False),
     synth.custom_moe("fl_empty_experts", T=20, H=256, I=384, E=16, w_cfg=507, x_cfg=507, expert_bias=True,
@@ -40,7 +42,7 @@ CASES = [
     # the fewest tokens that can need a second pass, and 52 tokens over 256 experts
     synth.custom_moe("fl_33", T=33, H=384, I=768, E=4, act=synth.ACT_GELU_ERF, w_cfg=511, x_cfg=511, out_f32=False),
     synth.custom_moe("fl_max_experts_52", T=52, H=128, I=256, E=256, w_cfg=512, x_cfg=512, logit_sigma=2.0),
-    # above 72 tokens: the routing, the tiled gate|up and down launches in sequence
+    # above 80 tokens: the routing, the tiled gate|up and down launches in sequence
     synth.custom_moe("fl_sequential", T=100, H=256, I=512, E=8, act=synth.ACT_GELU_ERF, w_cfg=509, x_cfg=509,
                      out_f32=False),
 ]

@@ -225,13 +225,13 @@ def test_moe_layer_parity(cfg):
     assert torch().equal(a, a3) and torch().equal(out, out3)
 
 
-# Token counts above 72 take the tiled kernel: tiles of 32, 64 or 256 rows (by the mean rows
+# Token counts above 80 take the tiled kernel: tiles of 32, 64 or 256 rows (by the mean rows
 # per expert) over each expert's segment (ragged last tiles, empty experts), 128-channel gate|up
 # tiles, 256-channel down tiles.
 PREFILL_CASES = [
     synth.custom_moe("pf_small", T=96, H=256, I=512, E=4, w_cfg=301, x_cfg=301),
-    # the fewest tokens that take the tiled kernel (72 take the streaming one)
-    synth.custom_moe("pf_first_tiled", T=73, H=384, I=256, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=307,
+    # the fewest tokens that take the tiled kernel (80 take the streaming one)
+    synth.custom_moe("pf_first_tiled", T=81, H=384, I=256, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=307,
                      x_cfg=307, logit_sigma=1.5),
     synth.custom_moe("pf_ragged", T=300, H=640, I=384, E=8, act=synth.ACT_GELU_ERF, out_f32=False, w_cfg=302,
                      x_cfg=302, logit_sigma=1.5),

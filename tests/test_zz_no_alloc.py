@@ -27,7 +27,7 @@ def _layer(cfg, T):
 @pytest.mark.parametrize("name,T1,T2,H,I,E", [
     # streaming kernel, I = 8192: two split-K slices of the down projection
     ("decode_split", 32, 5, 512, 8192, 8),
-    # the tiled kernel (more than 72 tokens), then a decode batch
+    # the tiled kernel (more than 80 tokens), then a decode batch
     ("tiled", 100, 20, 256, 512, 4),
 ])
 def test_noalloc_matches_workspace_call(name, T1, T2, H, I, E):

@@ -314,14 +314,15 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
   }
 }
 
-// The streaming kernel takes up to 72 tokens, the tiled kernel above. Measured whole layer
-// steps, us, streaming (two column tiles, passes of 32 rows) against tiled, with the router
-// as drawn and with a per-expert bias (the most rows of an expert in brackets): 72 tokens
-// Mixtral-shaped 156.2 against 166.5 (26), 179.9 against 184.1 (41); one GPU's 8-way share
-// of Grok-1 87.5 against 97.8 (25), 87.1 against 97.6 (30); Grok-1-shaped 486.2 against
-// 492.5 (25), 489.8 against 494.4 (30). At 80 and 88 tokens the Grok-1 shape is 1-4% slower
-// streamed and the biased routers tie or lose; at 128 streaming loses by 16-20%.
-constexpr int kStreamMaxTokens = 72;
+// The streaming kernel takes up to 80 tokens, the tiled kernel above. Measured whole layer
+// steps, us, streaming (two column tiles, passes of 32 rows, nontemporal weight stream)
+// against tiled, with the router as drawn and with a per-expert bias (the most rows of an
+// expert in brackets): 80 tokens Mixtral-shaped 158.9 against 168.3 (28), 176.3 against
+// 183.8 (48); one GPU's 8-way share of Grok-1 85.8 against 99.1 (24), 101.1 against 102.7
+// (37); Grok-1-shaped 490.8 against 492.8 (24), 517.6 against 527.7 (37). At 88 and 96
+// tokens the biased routers put more than 48 rows on an expert (a third pass) and streaming
+// loses by 9-12%; at 128 tokens it loses by 15-20% with either router.
+constexpr int kStreamMaxTokens = 80;
 bool decode_fits(int T) { return T <= kStreamMaxTokens; }
 
 // CUs of the current device, looked up once per device. Each slot is an atomic, so calls
