@@ -320,8 +320,8 @@ __global__ __launch_bounds__(kDecodeWaves * kWave) void moe_decode_kernel(MoeGem
 // expert in brackets): 80 tokens Mixtral-shaped 158.9 against 168.3 (28), 176.3 against
 // 183.8 (48); one GPU's 8-way share of Grok-1 85.8 against 99.1 (24), 101.1 against 102.7
 // (37); Grok-1-shaped 490.8 against 492.8 (24), 517.6 against 527.7 (37). At 88 and 96
-// tokens the biased routers put more than 48 rows on an expert (a third pass) and streaming
-// loses by 9-12%; at 128 tokens it loses by 15-20% with either router.
+// tokens the biased routers (largest experts of 52 to 56 rows, two passes) make streaming
+// lose by 9-12%; at 128 tokens it loses by 15-20% with either router.
 constexpr int kStreamMaxTokens = 80;
 bool decode_fits(int T) { return T <= kStreamMaxTokens; }
 
